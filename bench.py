@@ -1,0 +1,238 @@
+"""Benchmark of the GQE attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--cpu-seconds S]
+
+A step is one gqe_attn_fwd call over the whole layer (router, permutation,
+sparse Q, dense K/V, causal attention, weighted slot, output projection) on
+one batch of seeded synthetic input already resident in HBM. The default
+workload is the 32K-token long-context layer (B=1, T=32768, D=1024, G=8, M=2,
+k=1, d_h=64, bf16). Prints ONE JSON line with tokens/s, the attention kernel's
+MFMA roofline fraction (timed live with HIP events on the library's stream),
+the speedup over dense 16q/8kv GQA built from the same kernels, and the fp64
+oracle timed on the host's cores (a baseline only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GQE attn fwd tokens/s at T=32K + MFMA util %; speedup vs dense GQA 16q/8kv"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (fp32 layers run fp32 MFMA)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "sparse_moe_attention_amd", "csrc", "attention.hpp")
+
+
+def attn_flops(s, heads: int) -> float:
+    """Algorithmic flops of one attention launch: 2 products of 2*d flops per
+    (query, key) pair of the causal lower triangle (diagonal included)."""
+    return heads * s.B * 4.0 * s.d * s.T * (s.T + 1) / 2.0
+
+
+def layer_flops(s) -> float:
+    per_tok = (2 * s.D * s.G * s.M + 2 * s.D * (s.G * s.k + 1) * s.d + 4 * s.D * s.G * s.d
+               + 2 * (s.G * s.k + 2) * s.d * s.D + 2 * s.G * s.k * s.d)
+    return s.N * per_tok + attn_flops(s, s.G * s.k + 1)
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(config_id: int):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(f"config{config_id}")
+    if not entry or entry.get("attention_src_sha") != source_sha(ATTN_SRC):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(s, inp, target_s: float):
+    """The fp64 oracle on the host's cores, on a bounded sample of the same
+    layer: the dense per-token work (routing of all tokens, K/V projections)
+    runs in full; the per-row work (routed and shared queries, attention over
+    the whole causal prefix, slots, Wo) runs on R stratified rows and is
+    scaled by N/R. Returns the estimated whole-layer tokens/s."""
+    import numpy as np
+    import oracle.gqe_oracle as go
+    from workloads import sample_rows, to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(p.get("num_threads", 1)) for p in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    f = {k: to_f64(v) for k, v in inp.items()}
+    t = time.perf_counter()
+    go.route(f["x"], f["Wr"], f.get("br"), s.G, s.M, s.k)
+    go.project(f["x"], f["Wk"])
+    go.project(f["x"], f["Wv"])
+    t_fixed = time.perf_counter() - t
+    # calibrate the row count on a small sample, then fill the time budget
+    r0 = 16
+    t = time.perf_counter()
+    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, sample_rows(s, r0, 7))
+    per_row = max((time.perf_counter() - t - t_fixed) / r0, 1e-6)
+    R = int(min(s.N, max(r0, (target_s - t_fixed) / per_row)))
+    rows = sample_rows(s, R, 11)
+    t = time.perf_counter()
+    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, rows)
+    t_rows = time.perf_counter() - t
+    per_row = max((t_rows - t_fixed) / len(rows), 1e-9)
+    est = t_fixed + s.N * per_row
+    return {
+        "value": s.N / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: routing + K/V projection of all {s.N} tokens in full "
+                   f"({t_fixed:.2f} s), then {len(rows)} stratified rows of the full layer over their whole "
+                   f"causal prefix ({t_rows:.2f} s incl. the dense part again), per-row cost scaled to N; "
+                   f"estimated full-layer time {est:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the GQE forward runs on a single MI355X here; "
+              "run it with --gpus 1 (multi-GPU sharding is described in DESIGN.md, not built).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import sparse_moe_attention_amd as gq
+    from workloads import CONFIG_NAMES, config_inputs
+
+    gq.load()
+    torch.cuda.set_device(0)
+    s, inp = config_inputs(args.config)
+    steps = args.steps if args.steps is not None else {1: 50, 2: 50, 3: 20, 4: 20, 5: 3}[args.config]
+    dv = {k: (v.cuda().contiguous() if v is not None else None) for k, v in inp.items()}
+    dt = s.torch_dtype()
+    shape = gq.shape_from(s)
+    out = torch.empty(s.N, s.D, dtype=dt, device="cuda")
+    ws = torch.empty(gq.gqe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    dcode = gq.GQE_F32 if s.dtype == "f32" else gq.GQE_BF16
+
+    def mk_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record()
+        return evs
+
+    # ---- GQE: warmup, then K timed steps; events bracket the attention kernel
+    A0, A1 = 5, 6                    # events before / after the attention stage
+    for _ in range(args.warmup):
+        gq.gqe_attn_fwd(shape, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"],
+                        dv["Wo"], out, ws=ws)
+    step_ev = []
+    for _ in range(steps):
+        e = mk_events(2)
+        arr = [None] * (gq.GQE_N_STAGES + 1)
+        arr[A0], arr[A1] = e
+        step_ev.append((e, gq.event_array(arr)))
+    t0, t1 = mk_events(2)
+    torch.cuda.synchronize()
+    wall = time.perf_counter()
+    t0.record()
+    for _, arr in step_ev:
+        gq.gqe_attn_fwd_timed(shape, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"],
+                              dv["Wo"], out, arr, ws=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    ms_step = t0.elapsed_time(t1) / steps
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e, _ in step_ev) / steps
+
+    # one fully instrumented step for the per-stage breakdown (outside the timed region)
+    evs = mk_events(gq.GQE_N_STAGES + 1)
+    torch.cuda.synchronize()
+    gq.gqe_attn_fwd_timed(shape, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"],
+                          dv["Wo"], out, gq.event_array(evs), ws=ws)
+    torch.cuda.synchronize()
+    stage_ms = {n: round(evs[i].elapsed_time(evs[i + 1]), 4) for i, n in enumerate(gq.GQE_STAGE_NAMES)}
+
+    # ---- dense GQA over the same tensors
+    gqa = None
+    if not args.no_gqa:
+        wsg = torch.empty(gq.gqa_workspace_bytes(s.B, s.T, s.D, s.Hq, s.G, s.d, dcode), dtype=torch.uint8,
+                          device="cuda")
+        og = torch.empty_like(out)
+        for _ in range(args.warmup):
+            gq.gqa_attn_fwd(s.B, s.T, s.D, s.Hq, s.G, s.d, dcode, dv["x"], dv["Wq"], dv["Wk"], dv["Wv"],
+                            dv["Wo_gqa"], og, ws=wsg)
+        gev = []
+        for _ in range(steps):
+            e = mk_events(2)
+            arr = [None] * (gq.GQA_N_STAGES + 1)
+            arr[1], arr[2] = e
+            gev.append((e, gq.event_array(arr)))
+        g0, g1 = mk_events(2)
+        torch.cuda.synchronize()
+        g0.record()
+        for _, arr in gev:
+            gq.gqa_attn_fwd_timed(s.B, s.T, s.D, s.Hq, s.G, s.d, dcode, dv["x"], dv["Wq"], dv["Wk"], dv["Wv"],
+                                  dv["Wo_gqa"], og, arr, ws=wsg)
+        g1.record()
+        torch.cuda.synchronize()
+        gqa_ms = g0.elapsed_time(g1) / steps
+        gqa_attn_ms = sum(e[0].elapsed_time(e[1]) for e, _ in gev) / steps
+        gqa = {"tokens_per_s": s.N / (gqa_ms / 1e3), "ms_per_step": gqa_ms, "attention_ms": gqa_attn_ms,
+               "heads": f"{s.Hq}q/{s.G}kv", "speedup_gqe_over_gqa": gqa_ms / ms_step,
+               "attention_speedup": gqa_attn_ms / attn_ms}
+
+    peak = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
+    fl = attn_flops(s, s.G * s.k + 1)
+    achieved = fl / (attn_ms / 1e3) / 1e12
+    traffic = measured_traffic(args.config)
+    rec = {
+        "metric": METRIC,
+        "value": s.N / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded randn inputs and random-init weights of the layer's shape)",
+        "config": {"workload": CONFIG_NAMES[args.config], "B": s.B, "T": s.T, "D": s.D, "G": s.G, "M": s.M,
+                   "k": s.k, "d_h": s.d, "shared_kv_group": s.shared_kv_group, "tokens_per_step": s.N},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
+                     "algorithmic_flops_per_launch": fl, "avg_launch_ms": attn_ms},
+        "layer_mfma_frac": layer_flops(s) / (ms_step / 1e3) / 1e12 / peak,
+        "stage_ms": stage_ms,
+        "gqa_baseline": gqa,
+        "wall_s_timed_region": wall,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(s, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * gqe.h -- C ABI of libgqe.so: the forward pass of the Grouped Query Experts
+ * (GQE) attention layer on AMD Instinct MI355X (gfx950), plus the dense-GQA
+ * layer built from the same kernels.
+ *
+ * Sources (cited by title and section):
+ *   [GQE-x] "Grouped Query Experts: Mixture-of-Experts on GQA Self-Attention",
+ *           gist.science explainer of arXiv 2606.20945, technical summary,
+ *           "Architecture and routing" (grouped expert pool, conditional
+ *           activation of k experts per group, dense K/V path, output built
+ *           from hard concatenation, a renormalised weighted sum and an
+ *           always-on shared head) and "Experimental results" (16 query heads,
+ *           8 KV groups, k=1).
+ *   [GQE-n] FrontiersMind GQE news article (animattoys.com), part 4: each
+ *           expert owns its query projection; a lightweight router scores all
+ *           experts of every group and keeps the top k, best first; every
+ *           selected expert attends over its group's shared K/V; the hard-
+ *           concatenated outputs, the weighted-average slot and the shared
+ *           head are merged and then projected.
+ *   [GQA-w] aiboss88.com wiki "What is Grouped-Query Attention", "Mechanism":
+ *           query heads in groups share one K/V head.
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller allocates every buffer, device memory for all
+ *     tensors and for the workspace. The library allocates, frees and keeps
+ *     nothing between calls.
+ *   - Execution: all work is enqueued on `stream` (a hipStream_t; NULL means
+ *     the null stream) and the call returns without waiting. Outputs are
+ *     valid once the stream reaches that point. Calls keep no state and may
+ *     run concurrently on different streams with different workspaces.
+ *   - Layout: row-major and contiguous. Weights use the [out, in] convention
+ *     (y = x W^T). Token n = b*T + t. Every pointer must be 16-byte aligned.
+ *   - Types: with dtype GQE_BF16, x, the weights (except br), out and
+ *     slots_out are bf16; with GQE_F32 they are fp32. Router logits, router
+ *     offsets br and weights w are always fp32; idx and counts are int32.
+ *     Matrix products accumulate in fp32; the softmax state is fp32.
+ *   - Semantics fixed by the library: attention is causal (the diagonal is
+ *     included), scale 1/sqrt(d_h), no positional encoding; every batch
+ *     element is an independent sequence. Expert e = g*M + m owns rows
+ *     e*d_h .. e*d_h+d_h-1 of Wq. Top-k orders the experts of a group by
+ *     descending logit, ties to the lower index. Routing weights are the
+ *     per-group softmax probabilities of the picks, renormalised over all
+ *     G*k picks of the token (they sum to 1).
+ *   - Slot order of the merged output (and of Wo's input dimension):
+ *     [hard slots g-major, rank-minor (G*k*d_h) | weighted slot (d_h) |
+ *     shared slot (d_h)], i.e. (G*k+2)*d_h columns.
+ *   - Errors: negative status codes, never an exception or a print. Every
+ *     argument is checked before any HIP call, so errors are reported
+ *     without touching the device. A failed kernel launch returns
+ *     GQE_ERR_HIP. Inputs are never modified.
+ *   - Supported shapes: d_h in {32, 64}; D a positive multiple of 64;
+ *     1 <= k <= M <= 64; G*M <= 256; 0 <= shared_kv_group < G; B, T >= 1;
+ *     B*T*max(G*k, 1) < 2^31.
+ */
+#ifndef GQE_H
+#define GQE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQE_OK = 0,
+    GQE_ERR_NULL = -1,         /* a required pointer is NULL */
+    GQE_ERR_SHAPE = -2,        /* an inconsistent or out-of-range size */
+    GQE_ERR_UNSUPPORTED = -3,  /* a valid size this build does not handle (d_h, D, M, G*M) */
+    GQE_ERR_WORKSPACE = -4,    /* ws_bytes smaller than the *_workspace_bytes figure */
+    GQE_ERR_ALIGN = -5,        /* a pointer not aligned to 16 bytes */
+    GQE_ERR_HIP = -6           /* the HIP runtime reported an error at launch */
+} gqe_status;
+
+typedef enum { GQE_BF16 = 0, GQE_F32 = 1 } gqe_dtype;
+
+/* One GQE layer. B batch, T sequence length, D model width, G KV groups,
+ * M query experts per group, k experts picked per group, d_h head width,
+ * shared_kv_group the KV group the always-on shared head reads,
+ * dtype a gqe_dtype. */
+typedef struct {
+    int64_t B, T, D;
+    int32_t G, M, k, d_h, shared_kv_group;
+    int32_t dtype;
+} gqe_shape;
+
+/* Bytes of device workspace gqe_route, gqe_attn_fwd_routed and gqe_attn_fwd
+ * need for this shape (one figure covers all three). Returns 0 if the shape
+ * is invalid or unsupported. */
+size_t gqe_workspace_bytes(const gqe_shape* s);
+
+/* Router only. [GQE-x] "Architecture and routing" (conditional activation);
+ * [GQE-n] part 4 (score every expert of every group, keep the top k).
+ *   x      [B*T, D]            input activations
+ *   Wr     [G*M, D]            router weight
+ *   br     [G*M] fp32 or NULL  per-expert logit offset
+ *   idx    [B*T, G, k] int32   out: picked expert m of group g, rank r (best first)
+ *   w      [B*T, G, k] fp32    out: renormalised routing weights
+ *   logits [B*T, G*M] fp32     out (NULL to skip): x Wr^T + br
+ *   counts [G*M] int32         out (NULL to skip): tokens routed to each expert
+ *   ws, ws_bytes               workspace of at least gqe_workspace_bytes(s) */
+gqe_status gqe_route(const gqe_shape* s, const void* x, const void* Wr, const float* br,
+                     int32_t* idx, float* w, float* logits, int32_t* counts,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Everything after the router, with the routing given by the caller.
+ * [GQE-x] "Architecture and routing" (dense K/V path; Q only for the picked
+ * experts; hard concatenation; renormalised weighted sum; shared head);
+ * [GQE-n] part 4 (each picked expert attends over its group's K/V; the three
+ * parts are merged and projected).
+ *   x       [B*T, D]
+ *   Wq      [G*M*d_h, D]          query projection of every expert
+ *   Wk, Wv  [G*d_h, D]            key and value projections of every group
+ *   Wq_sh   [d_h, D]              query projection of the shared head
+ *   Wo      [D, (G*k+2)*d_h]      output projection over the merged slots
+ *   idx     [B*T, G, k] int32     picked experts, each in [0, M), distinct
+ *                                 within a group; an entry outside [0, M) is
+ *                                 skipped and its hard slot holds unspecified
+ *                                 values (no out-of-bounds access results)
+ *   w       [B*T, G, k] fp32      weights of the weighted slot
+ *   out     [B*T, D]              out: layer output
+ *   slots_out [B*T, (G*k+2)*d_h]  out (NULL to skip): the merged slots */
+gqe_status gqe_attn_fwd_routed(const gqe_shape* s, const void* x, const void* Wq, const void* Wk,
+                               const void* Wv, const void* Wq_sh, const void* Wo,
+                               const int32_t* idx, const float* w, void* out, void* slots_out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* The whole GQE layer: router, sparse Q, dense K/V, causal attention of the
+ * picked experts and the shared head, merged slots, output projection.
+ * [GQE-x] "Architecture and routing"; [GQE-n] part 4.
+ *   Arguments as in gqe_route and gqe_attn_fwd_routed.
+ *   idx_out, w_out [B*T, G, k]    out (NULL to skip): the routing used */
+gqe_status gqe_attn_fwd(const gqe_shape* s, const void* x, const void* Wr, const float* br,
+                        const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh,
+                        const void* Wo, void* out, int32_t* idx_out, float* w_out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Dense GQA baseline over the same kernels: Hq query heads, G KV groups, head
+ * h reads group h / (Hq/G), every head active on every token.
+ * [GQA-w] "Mechanism"; [GQE-x] "Experimental results" (the 16-query, 8-KV
+ * GQA model GQE is compared with).
+ *   x [B*T, D]; Wq [Hq*d_h, D]; Wk, Wv [G*d_h, D]; Wo [D, Hq*d_h]; out [B*T, D].
+ * Returns 0 (workspace) or GQE_ERR_SHAPE unless Hq is a positive multiple of
+ * G with Hq <= 256. */
+size_t gqa_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t Hq, int32_t G, int32_t d_h,
+                           int32_t dtype);
+gqe_status gqa_attn_fwd(int64_t B, int64_t T, int64_t D, int32_t Hq, int32_t G, int32_t d_h,
+                        int32_t dtype, const void* x, const void* Wq, const void* Wk,
+                        const void* Wv, const void* Wo, void* out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Instrumented forms of gqe_attn_fwd and gqa_attn_fwd, for measurement:
+ * same arguments, same results, and `events` (may be NULL) points at
+ * GQE_N_STAGES+1 (resp. GQA_N_STAGES+1) hipEvent_t handles, each NULL or an
+ * event the caller created. Event i is recorded on `stream` just before
+ * stage i is enqueued, the last one after the final stage, so the time
+ * between events i and i+1 is stage i's device time. Stages of the GQE
+ * forward: 0 projection (K, V, Q_sh, router logits), 1 route, 2 scan,
+ * 3 scatter, 4 sparse Q grouped GEMM, 5 attention, 6 weighted slot,
+ * 7 output projection. Stages of the GQA forward: 0 projection (Q, K, V),
+ * 1 attention, 2 output projection. */
+#define GQE_N_STAGES 8
+#define GQA_N_STAGES 3
+gqe_status gqe_attn_fwd_timed(const gqe_shape* s, const void* x, const void* Wr, const float* br,
+                              const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh,
+                              const void* Wo, void* out, int32_t* idx_out, float* w_out,
+                              void* ws, size_t ws_bytes, void* stream, void* const* events);
+gqe_status gqa_attn_fwd_timed(int64_t B, int64_t T, int64_t D, int32_t Hq, int32_t G, int32_t d_h,
+                              int32_t dtype, const void* x, const void* Wq, const void* Wk,
+                              const void* Wv, const void* Wo, void* out,
+                              void* ws, size_t ws_bytes, void* stream, void* const* events);
+
+/* A static, NUL-terminated description of a status code. */
+const char* gqe_status_str(gqe_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQE_H */

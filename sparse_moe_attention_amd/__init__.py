@@ -1,0 +1,200 @@
+"""Python binding of libgqe.so, the gfx950 GQE attention forward library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. Torch supplies device memory and the current stream. If libgqe.so is
+missing the import succeeds but every call raises; there is no fallback.
+
+Entry points (same names as the C ABI in include/gqe.h):
+    gqe_workspace_bytes(shape)
+    gqe_route(shape, x, Wr, br, idx, w, logits=None, counts=None, ws=None)
+    gqe_attn_fwd_routed(shape, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, slots_out=None, ws=None)
+    gqe_attn_fwd(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out=None, w_out=None, ws=None)
+    gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype)
+    gqa_attn_fwd(B, T, D, Hq, G, d_h, dtype, x, Wq, Wk, Wv, Wo, out, ws=None)
+    gqe_status_str(code)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgqe.so")
+
+GQE_BF16, GQE_F32 = 0, 1
+GQE_N_STAGES, GQA_N_STAGES = 8, 3
+GQE_STAGE_NAMES = ("proj_kv_qsh_router", "route", "scan", "scatter", "grouped_q", "attention",
+                   "weighted_slot", "out_proj")
+GQA_STAGE_NAMES = ("proj_qkv", "attention", "out_proj")
+
+STATUS = {
+    0: "GQE_OK", -1: "GQE_ERR_NULL", -2: "GQE_ERR_SHAPE", -3: "GQE_ERR_UNSUPPORTED",
+    -4: "GQE_ERR_WORKSPACE", -5: "GQE_ERR_ALIGN", -6: "GQE_ERR_HIP",
+}
+
+
+class GqeShape(ctypes.Structure):
+    """Mirror of the C struct gqe_shape."""
+    _fields_ = [
+        ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
+        ("G", ctypes.c_int32), ("M", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("d_h", ctypes.c_int32), ("shared_kv_group", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+class GqeError(RuntimeError):
+    def __init__(self, code: int, text: str):
+        super().__init__(text)
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgqe.so (once) and declare its signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m sparse_moe_attention_amd.build` "
+            "(the library has no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    SH = ctypes.POINTER(GqeShape)
+    lib.gqe_workspace_bytes.argtypes = [SH]
+    lib.gqe_workspace_bytes.restype = S
+    lib.gqe_route.argtypes = [SH, P, P, P, P, P, P, P, P, S, P]
+    lib.gqe_route.restype = ctypes.c_int
+    lib.gqe_attn_fwd_routed.argtypes = [SH, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gqe_attn_fwd_routed.restype = ctypes.c_int
+    lib.gqe_attn_fwd.argtypes = [SH, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gqe_attn_fwd.restype = ctypes.c_int
+    lib.gqa_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, I32, I32]
+    lib.gqa_workspace_bytes.restype = S
+    lib.gqa_attn_fwd.argtypes = [I64, I64, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, S, P]
+    lib.gqa_attn_fwd.restype = ctypes.c_int
+    lib.gqe_attn_fwd_timed.argtypes = [SH, P, P, P, P, P, P, P, P, P, P, P, P, S, P, P]
+    lib.gqe_attn_fwd_timed.restype = ctypes.c_int
+    lib.gqa_attn_fwd_timed.argtypes = [I64, I64, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, S, P, P]
+    lib.gqa_attn_fwd_timed.restype = ctypes.c_int
+    lib.gqe_status_str.argtypes = [ctypes.c_int]
+    lib.gqe_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def gqe_status_str(code: int) -> str:
+    return load().gqe_status_str(code).decode()
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise GqeError(code, gqe_status_str(code))
+
+
+def make_shape(B, T, D, G, M, k, d_h, shared_kv_group=0, dtype=GQE_BF16) -> GqeShape:
+    return GqeShape(B, T, D, G, M, k, d_h, shared_kv_group, dtype)
+
+
+def shape_from(s) -> GqeShape:
+    """GqeShape from any object with B, T, D, G, M, k, d (and optional dtype
+    "bf16"/"f32", shared_kv_group) attributes."""
+    dt = GQE_F32 if getattr(s, "dtype", "bf16") in ("f32", GQE_F32) else GQE_BF16
+    return make_shape(s.B, s.T, s.D, s.G, s.M, s.k, s.d, getattr(s, "shared_kv_group", 0), dt)
+
+
+def _ptr(t):
+    """Device address of a torch tensor (None -> NULL). Refuses host tensors
+    and non-contiguous views; the library does the remaining checks."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libgqe takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libgqe takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _workspace(nbytes: int, like):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+
+
+def gqe_workspace_bytes(shape: GqeShape) -> int:
+    return int(load().gqe_workspace_bytes(ctypes.byref(shape)))
+
+
+def gqe_route(shape, x, Wr, br, idx, w, logits=None, counts=None, ws=None, stream=None):
+    lib = load()
+    if ws is None:
+        ws = _workspace(gqe_workspace_bytes(shape), x)
+    _check(lib.gqe_route(ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(br), _ptr(idx), _ptr(w),
+                         _ptr(logits), _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gqe_attn_fwd_routed(shape, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, slots_out=None, ws=None, stream=None):
+    lib = load()
+    if ws is None:
+        ws = _workspace(gqe_workspace_bytes(shape), x)
+    _check(lib.gqe_attn_fwd_routed(ctypes.byref(shape), _ptr(x), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wq_sh),
+                                   _ptr(Wo), _ptr(idx), _ptr(w), _ptr(out), _ptr(slots_out), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+
+
+def gqe_attn_fwd(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out=None, w_out=None, ws=None, stream=None):
+    lib = load()
+    if ws is None:
+        ws = _workspace(gqe_workspace_bytes(shape), x)
+    _check(lib.gqe_attn_fwd(ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(br), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                            _ptr(Wq_sh), _ptr(Wo), _ptr(out), _ptr(idx_out), _ptr(w_out), _ptr(ws),
+                            ws.numel(), _stream(stream)))
+
+
+def gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype=GQE_BF16) -> int:
+    return int(load().gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype))
+
+
+def gqa_attn_fwd(B, T, D, Hq, G, d_h, dtype, x, Wq, Wk, Wv, Wo, out, ws=None, stream=None):
+    lib = load()
+    if ws is None:
+        ws = _workspace(gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype), x)
+    _check(lib.gqa_attn_fwd(B, T, D, Hq, G, d_h, dtype, _ptr(x), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
+                            _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def event_array(events):
+    """ctypes array of raw hipEvent_t handles from torch.cuda.Event objects
+    (None entries stay NULL). Each event must have been recorded once."""
+    arr = (ctypes.c_void_p * len(events))()
+    for i, e in enumerate(events):
+        arr[i] = None if e is None else e.cuda_event
+    return arr
+
+
+def gqe_attn_fwd_timed(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, events, idx_out=None, w_out=None,
+                       ws=None, stream=None):
+    """gqe_attn_fwd plus a hipEvent record before every stage (events: a
+    ctypes array from event_array, GQE_N_STAGES + 1 entries)."""
+    lib = load()
+    if ws is None:
+        ws = _workspace(gqe_workspace_bytes(shape), x)
+    _check(lib.gqe_attn_fwd_timed(ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(br), _ptr(Wq), _ptr(Wk),
+                                  _ptr(Wv), _ptr(Wq_sh), _ptr(Wo), _ptr(out), _ptr(idx_out), _ptr(w_out),
+                                  _ptr(ws), ws.numel(), _stream(stream), events))
+
+
+def gqa_attn_fwd_timed(B, T, D, Hq, G, d_h, dtype, x, Wq, Wk, Wv, Wo, out, events, ws=None, stream=None):
+    lib = load()
+    if ws is None:
+        ws = _workspace(gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype), x)
+    _check(lib.gqa_attn_fwd_timed(B, T, D, Hq, G, d_h, dtype, _ptr(x), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
+                                  _ptr(out), _ptr(ws), ws.numel(), _stream(stream), events))

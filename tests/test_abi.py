@@ -1,0 +1,120 @@
+"""The C ABI of libgqe.so on the CPU: it loads without a GPU, exports every
+function include/gqe.h declares, and reports every validation status code
+before any HIP call (host addresses below are never dereferenced)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_attention_amd as gq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqe.h")
+
+A = 0x10000          # a 16-byte aligned host address (never touched)
+BAD = 0x10008        # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq[ae]_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gq.load()
+
+
+def shape(**kw):
+    base = dict(B=1, T=128, D=128, G=2, M=2, k=1, d_h=32, shared_kv_group=0, dtype=gq.GQE_BF16)
+    base.update(kw)
+    return gq.GqeShape(**base)
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) >= {"gqe_workspace_bytes", "gqe_route", "gqe_attn_fwd_routed", "gqe_attn_fwd",
+                          "gqa_workspace_bytes", "gqa_attn_fwd", "gqe_status_str"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in gq.STATUS.items():
+        assert gq.gqe_status_str(code).startswith(name)
+    assert "unknown" in gq.gqe_status_str(-99)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=3), -2), (dict(k=0), -2), (dict(B=0), -2), (dict(T=0), -2), (dict(G=0), -2),
+    (dict(shared_kv_group=2), -2), (dict(shared_kv_group=-1), -2),
+    (dict(d_h=48), -3), (dict(D=100), -3), (dict(dtype=7), -3), (dict(M=65, k=1), -3),
+    (dict(G=17, M=16), -3), (dict(B=1 << 20, T=1 << 20), -2),
+])
+def test_shape_errors(lib, kw, code):
+    s = shape(**kw)
+    assert lib.gqe_workspace_bytes(ctypes.byref(s)) == 0
+    rc = lib.gqe_attn_fwd(ctypes.byref(s), A, A, None, A, A, A, A, A, A, None, None, A, 1 << 40, None)
+    assert rc == code
+    rc = lib.gqe_route(ctypes.byref(s), A, A, None, A, A, None, None, A, 1 << 40, None)
+    assert rc == code
+
+
+def test_null_shape(lib):
+    assert lib.gqe_workspace_bytes(None) == 0
+    assert lib.gqe_attn_fwd(None, A, A, None, A, A, A, A, A, A, None, None, A, 1 << 40, None) == -1
+
+
+def test_null_pointers(lib):
+    s = shape()
+    big = 1 << 40
+    assert lib.gqe_attn_fwd(ctypes.byref(s), None, A, None, A, A, A, A, A, A, None, None, A, big, None) == -1
+    assert lib.gqe_attn_fwd(ctypes.byref(s), A, A, None, A, A, A, A, A, None, None, None, A, big, None) == -1
+    assert lib.gqe_route(ctypes.byref(s), A, A, None, None, A, None, None, A, big, None) == -1
+    assert lib.gqe_attn_fwd_routed(ctypes.byref(s), A, A, A, A, A, A, None, A, A, None, A, big, None) == -1
+    assert lib.gqa_attn_fwd(1, 128, 128, 4, 2, 32, 0, A, A, A, A, A, None, A, big, None) == -1
+
+
+def test_alignment(lib):
+    s = shape()
+    big = 1 << 40
+    assert lib.gqe_attn_fwd(ctypes.byref(s), BAD, A, None, A, A, A, A, A, A, None, None, A, big, None) == -5
+    assert lib.gqe_attn_fwd(ctypes.byref(s), A, A, BAD, A, A, A, A, A, A, None, None, A, big, None) == -5
+    assert lib.gqe_route(ctypes.byref(s), A, A, None, A, A, BAD, None, A, big, None) == -5
+    assert lib.gqe_attn_fwd_routed(ctypes.byref(s), A, A, A, A, A, A, A, A, A, BAD, A, big, None) == -5
+    assert lib.gqa_attn_fwd(1, 128, 128, 4, 2, 32, 0, A, A, A, A, A, A, BAD, big, None) == -5
+
+
+def test_workspace_too_small(lib):
+    s = shape()
+    need = lib.gqe_workspace_bytes(ctypes.byref(s))
+    assert need > 0
+    assert lib.gqe_attn_fwd(ctypes.byref(s), A, A, None, A, A, A, A, A, A, None, None, A, need - 1, None) == -4
+    assert lib.gqe_route(ctypes.byref(s), A, A, None, A, A, None, None, A, need - 1, None) == -4
+    assert lib.gqe_attn_fwd_routed(ctypes.byref(s), A, A, A, A, A, A, A, A, A, None, A, need - 1, None) == -4
+    g = lib.gqa_workspace_bytes(1, 128, 128, 4, 2, 32, 0)
+    assert g > 0
+    assert lib.gqa_attn_fwd(1, 128, 128, 4, 2, 32, 0, A, A, A, A, A, A, A, g - 1, None) == -4
+
+
+def test_gqa_shape_errors(lib):
+    assert lib.gqa_workspace_bytes(1, 128, 128, 5, 2, 32, 0) == 0          # Hq not a multiple of G
+    assert lib.gqa_attn_fwd(1, 128, 128, 5, 2, 32, 0, A, A, A, A, A, A, A, 1 << 40, None) == -2
+    assert lib.gqa_attn_fwd(1, 128, 128, 4, 2, 48, 0, A, A, A, A, A, A, A, 1 << 40, None) == -3
+    assert lib.gqa_workspace_bytes(1, 128, 128, 512, 2, 32, 0) == 0        # Hq > 256
+
+
+def test_workspace_monotone_in_tokens(lib):
+    prev = 0
+    for T in (1, 7, 64, 65, 128, 1000, 4096, 32768):
+        s = shape(T=T, D=1024, G=8, M=2, d_h=64)
+        n = lib.gqe_workspace_bytes(ctypes.byref(s))
+        assert n > prev
+        prev = n
+    # the extreme-context layer fits comfortably in one MI355X's 288 GB
+    s = shape(T=1 << 20, D=1024, G=8, M=2, d_h=64)
+    assert lib.gqe_workspace_bytes(ctypes.byref(s)) < 8 << 30

@@ -1,0 +1,167 @@
+"""GPU parity of libgqe.so against the fp64 oracle, through the C ABI.
+
+Per stage: router logits (fp32 vs fp64), idx (bit-exact except near-tie
+rows), w, per-expert counts, merged slots, and the layer output. Small shapes
+are compared element by element over the whole tensor; the large layers
+(32K and 1M tokens) on sampled rows that the oracle computes one by one.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gqe_oracle as go
+import sparse_moe_attention_amd as gq
+from tests import harness as H
+from workloads import CONFIGS, Shape, config_inputs, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+# Shapes that span several tiles, ragged tails and the degenerate cases.
+CASES = {
+    "ragged_bias_k2": Shape(B=3, T=200, D=128, G=3, M=3, k=2, d=32, router_bias=True, shared_kv_group=1),
+    "fp32_k3_of_4": Shape(B=2, T=77, D=64, G=2, M=4, k=3, d=64, dtype="f32"),
+    "single_token": Shape(B=2, T=1, D=64, G=2, M=2, k=1, d=64),
+    "one_group": Shape(B=1, T=300, D=192, G=1, M=4, k=2, d=64),
+    "one_expert": Shape(B=1, T=130, D=64, G=4, M=1, k=1, d=32),
+    "all_experts": Shape(B=2, T=150, D=128, G=2, M=3, k=3, d=64),
+    "multi_tile": Shape(B=2, T=1000, D=256, G=8, M=2, k=1, d=64),
+    "wide_pool": Shape(B=1, T=260, D=128, G=4, M=16, k=4, d=32, router_bias=True),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gq.load()
+    torch.cuda.set_device(0)
+
+
+def check_routing(s, f, dv, tag):
+    """gqe_route against the oracle; returns (GPU idx, GPU w, oracle routing, near-tie mask)."""
+    logits_ref, sel_ref, w_ref = H.oracle_routing(f, s)
+    near = H.near_tie_rows(logits_ref, s)
+    o = H.alloc_outputs(s)
+    lg = torch.empty(s.N, s.G * s.M, dtype=torch.float32, device="cuda")
+    counts = torch.empty(s.G * s.M, dtype=torch.int32, device="cuda")
+    gq.gqe_route(gq.shape_from(s), dv["x"], dv["Wr"], dv["br"], o["idx"], o["w"], lg, counts)
+    torch.cuda.synchronize()
+    lg_n = lg.cpu().numpy().astype(np.float64)
+    lerr = np.abs(lg_n - logits_ref) / np.maximum(1.0, np.abs(logits_ref))
+    assert lerr.max() <= H.LOGIT_REL, (tag, "logits", lerr.max())
+    idx = o["idx"].cpu().numpy()
+    w = o["w"].cpu().numpy().astype(np.float64)
+    bad = (idx != sel_ref).any(axis=(1, 2))
+    assert not (bad & ~near).any(), (tag, "idx mismatch off near-ties", np.nonzero(bad & ~near)[0][:10])
+    ok = ~bad
+    werr = np.abs(w[ok] - w_ref[ok]).max() if ok.any() else 0.0
+    assert werr <= H.W_ABS, (tag, "w", werr)
+    e = (idx.reshape(s.N, s.G, s.k) + (np.arange(s.G) * s.M)[None, :, None]).reshape(-1)
+    assert (counts.cpu().numpy() == np.bincount(e, minlength=s.G * s.M)).all(), (tag, "counts")
+    assert (counts.cpu().numpy().sum() == s.N * s.G * s.k)
+    return idx, w, (logits_ref, sel_ref, w_ref), near, bad
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_small_layer_full_parity(name):
+    s = CASES[name]
+    inp = make_inputs(s, seed=7 + len(name))
+    f = H.f64_inputs(inp)
+    dv = H.to_device(inp)
+    print(f"[case {name}] {s}", flush=True)
+    idx, w, (lref, sref, wref), near, bad = check_routing(s, f, dv, name)
+    ref = go.gqe_forward(f, s.G, s.M, s.k, s.d, s.B, s.T, shared_kv_group=s.shared_kv_group)
+
+    # Full path: idx_out must equal gqe_route's, out must match on every row
+    # whose routing agrees with the oracle.
+    o = H.alloc_outputs(s)
+    H.run_gqe(s, dv, o)
+    torch.cuda.synchronize()
+    assert (o["idx"].cpu().numpy() == idx).all()
+    assert (o["w"].cpu().numpy() == w.astype(np.float32)).all()
+    got = H.np32(o["out"])
+    keep = ~bad
+    err, bound = H.out_error(got[keep], ref["out"][keep])
+    assert err <= bound, (name, "out", err, bound)
+
+    # Routed path with the oracle's routing injected: slots and out on every row.
+    out2 = torch.empty_like(o["out"])
+    slots = torch.empty(s.N, s.slots * s.d, dtype=s.torch_dtype(), device="cuda")
+    H.run_gqe_routed(s, dv, torch.from_numpy(sref.astype(np.int32)).cuda(),
+                     torch.from_numpy(wref.astype(np.float32)).cuda(), out2, slots)
+    torch.cuda.synchronize()
+    err, bound = H.out_error(H.np32(slots), ref["C"])
+    assert err <= bound, (name, "slots", err, bound)
+    err, bound = H.out_error(H.np32(out2), ref["out"])
+    assert err <= bound, (name, "routed out", err, bound)
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_config_full_parity(cid):
+    s, inp = config_inputs(cid)
+    print(f"[config {cid}] {s}", flush=True)
+    f = H.f64_inputs(inp)
+    dv = H.to_device(inp)
+    idx, w, (lref, sref, wref), near, bad = check_routing(s, f, dv, f"config{cid}")
+    ref = go.gqe_forward(f, s.G, s.M, s.k, s.d, s.B, s.T)
+    o = H.alloc_outputs(s)
+    H.run_gqe(s, dv, o)
+    torch.cuda.synchronize()
+    got = H.np32(o["out"])
+    err, bound = H.out_error(got[~bad], ref["out"][~bad])
+    print(f"[config {cid}] out max err {err:.3e} bound {bound:.3e}; near-tie rows {int(near.sum())}, "
+          f"mismatched {int(bad.sum())}", flush=True)
+    assert err <= bound
+    out2 = torch.empty_like(o["out"])
+    H.run_gqe_routed(s, dv, torch.from_numpy(sref.astype(np.int32)).cuda(),
+                     torch.from_numpy(wref.astype(np.float32)).cuda(), out2)
+    torch.cuda.synchronize()
+    err, bound = H.out_error(H.np32(out2), ref["out"])
+    assert err <= bound, ("routed", err, bound)
+    # dense GQA over the same tensors
+    ga = go.gqa_forward(dict(x=f["x"], Wq=f["Wq"], Wk=f["Wk"], Wv=f["Wv"], Wo=f["Wo_gqa"]),
+                        s.G, s.Hq, s.d, s.B, s.T)
+    og = torch.empty_like(o["out"])
+    H.run_gqa(s, dv, og)
+    torch.cuda.synchronize()
+    err, bound = H.out_error(H.np32(og), ga["out"])
+    assert err <= bound, ("gqa", err, bound)
+
+
+@pytest.mark.parametrize("cid,n_rows", [(3, 128), (4, 128), pytest.param(5, 64, marks=pytest.mark.timeout(600))])
+def test_config_sampled_parity(cid, n_rows):
+    s, inp = config_inputs(cid)
+    print(f"[config {cid}] {s}", flush=True)
+    f = H.f64_inputs(inp)
+    dv = H.to_device(inp)
+    del inp
+    idx, w, (lref, sref, wref), near, bad = check_routing(s, f, dv, f"config{cid}")
+    rows = sample_rows(s, n_rows, seed=1000 + cid)
+    ref = go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, rows)
+    o = H.alloc_outputs(s)
+    H.run_gqe(s, dv, o)
+    torch.cuda.synchronize()
+    got = H.np32(o["out"][torch.from_numpy(rows).cuda()])
+    keep = ~bad[rows]
+    err, bound = H.out_error(got[keep], ref["out"][keep])
+    print(f"[config {cid}] sampled out max err {err:.3e} bound {bound:.3e}; near-tie rows "
+          f"{int(near.sum())}, mismatched {int(bad.sum())}", flush=True)
+    assert err <= bound
+    # routed path with the oracle's routing
+    out2 = torch.empty_like(o["out"])
+    H.run_gqe_routed(s, dv, torch.from_numpy(sref.astype(np.int32)).cuda(),
+                     torch.from_numpy(wref.astype(np.float32)).cuda(), out2)
+    torch.cuda.synchronize()
+    got2 = H.np32(out2[torch.from_numpy(rows).cuda()])
+    err, bound = H.out_error(got2, ref["out"])
+    assert err <= bound, ("routed", err, bound)
+    if cid == 3:
+        gref = go.gqa_rows(dict(x=f["x"], Wq=f["Wq"], Wk=f["Wk"], Wv=f["Wv"], Wo=f["Wo_gqa"]),
+                           s.G, s.Hq, s.d, s.B, s.T, rows)
+        og = torch.empty_like(o["out"])
+        H.run_gqa(s, dv, og)
+        torch.cuda.synchronize()
+        err, bound = H.out_error(H.np32(og[torch.from_numpy(rows).cuda()]), gref["out"])
+        assert err <= bound, ("gqa", err, bound)

@@ -1,0 +1,111 @@
+"""GPU properties of libgqe.so that hold at any size: tie-breaking, the k=M
+reduction to dense GQA, causality, batch independence, expert segment sizes
+and run-to-run determinism. All calls go through the C ABI."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_moe_attention_amd as gq
+from tests import harness as H
+from workloads import Shape, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gq.load()
+
+
+def test_ties_go_to_lowest_index():
+    s = Shape(B=2, T=300, D=128, G=4, M=4, k=2, d=64)
+    inp = make_inputs(s, 21)
+    inp["Wr"] = torch.zeros_like(inp["Wr"])
+    dv = H.to_device(inp)
+    o = H.alloc_outputs(s)
+    gq.gqe_route(gq.shape_from(s), dv["x"], dv["Wr"], None, o["idx"], o["w"])
+    torch.cuda.synchronize()
+    assert (o["idx"].cpu().numpy() == np.arange(s.k)[None, None, :]).all()
+    assert np.abs(o["w"].cpu().numpy() - 1.0 / (s.G * s.k)).max() <= 1e-7
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_k_equals_M_uniform_router_is_gqa(dtype):
+    s = Shape(B=2, T=260, D=128, G=4, M=2, k=2, d=64, dtype=dtype)
+    inp = make_inputs(s, 22)
+    inp["Wr"] = torch.zeros_like(inp["Wr"])
+    z = torch.zeros(s.D, 2 * s.d, dtype=inp["Wo"].dtype)
+    inp["Wo"] = torch.cat([inp["Wo_gqa"], z], dim=1).contiguous()
+    dv = H.to_device(inp)
+    o = H.alloc_outputs(s)
+    H.run_gqe(s, dv, o)
+    og = torch.empty_like(o["out"])
+    H.run_gqa(s, dv, og)
+    torch.cuda.synchronize()
+    a, b = H.np32(o["out"]), H.np32(og)
+    err = np.abs(a - b).max()
+    assert err <= 1e-2 * np.abs(b).max() + 1e-3, err
+
+
+def test_causality_bit_exact():
+    s = Shape(B=1, T=700, D=128, G=4, M=2, k=1, d=64)
+    inp = make_inputs(s, 23)
+    dv = H.to_device(inp)
+    o1 = H.alloc_outputs(s)
+    H.run_gqe(s, dv, o1)
+    cut = 333
+    gen = torch.Generator().manual_seed(5)
+    x2 = inp["x"].clone()
+    x2[cut:] = torch.randn(x2[cut:].shape, generator=gen).to(x2.dtype)
+    dv2 = dict(dv)
+    dv2["x"] = x2.cuda()
+    o2 = H.alloc_outputs(s)
+    H.run_gqe(s, dv2, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1["out"][:cut], o2["out"][:cut])
+    assert not torch.equal(o1["out"][cut:], o2["out"][cut:])
+
+
+def test_batch_independence_bit_exact():
+    s = Shape(B=3, T=190, D=128, G=2, M=3, k=2, d=32, router_bias=True)
+    inp = make_inputs(s, 24)
+    dv = H.to_device(inp)
+    o = H.alloc_outputs(s)
+    H.run_gqe(s, dv, o)
+    s1 = Shape(B=1, T=190, D=128, G=2, M=3, k=2, d=32, router_bias=True)
+    for b in range(s.B):
+        d1 = dict(dv)
+        d1["x"] = dv["x"][b * s.T:(b + 1) * s.T].contiguous()
+        o1 = H.alloc_outputs(s1)
+        H.run_gqe(s1, d1, o1)
+        torch.cuda.synchronize()
+        assert torch.equal(o["out"][b * s.T:(b + 1) * s.T], o1["out"]), b
+
+
+def test_segments_and_determinism():
+    s = Shape(B=2, T=4096, D=256, G=8, M=4, k=2, d=64, router_bias=True)
+    inp = make_inputs(s, 25)
+    dv = H.to_device(inp)
+    ws = torch.empty(gq.gqe_workspace_bytes(gq.shape_from(s)), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        o = H.alloc_outputs(s)
+        H.run_gqe(s, dv, o, ws=ws)
+        outs.append(o)
+    counts = torch.empty(s.G * s.M, dtype=torch.int32, device="cuda")
+    idx = torch.empty_like(outs[0]["idx"])
+    w = torch.empty_like(outs[0]["w"])
+    gq.gqe_route(gq.shape_from(s), dv["x"], dv["Wr"], dv["br"], idx, w, None, counts)
+    torch.cuda.synchronize()
+    for key in ("out", "idx", "w"):
+        assert torch.equal(outs[0][key], outs[1][key]), key
+    e = (idx.cpu().numpy() + (np.arange(s.G) * s.M)[None, :, None]).reshape(-1)
+    c = counts.cpu().numpy()
+    assert (c == np.bincount(e, minlength=s.G * s.M)).all()
+    assert c.sum() == s.N * s.G * s.k
+    # the biased router really skews the loads
+    assert c.max() > 2 * c.min()
