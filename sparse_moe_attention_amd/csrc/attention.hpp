@@ -7,14 +7,25 @@
 // GQA baseline runs one per query head. Both are the same kernel: a head is a
 // query source (base, row stride), a KV group and an output column.
 //
-// Per workgroup: one head, one sequence, BQ=128 queries (4 waves x 32).
+// Work split: one workgroup = one head, one sequence, NW waves x QW queries.
 // K/V tiles of 64 keys are staged in double-buffered LDS and shared by the
-// four waves. Scores are computed transposed, S^T = K Q^T, so that after the
-// softmax each lane already holds, for its query column, the key slots the
-// second product O^T = V^T P^T wants as its B operand: no shuffles between
-// the two MFMA stages. V is kept transposed in HBM ([group][d][token]) so its
-// A operand reads contiguous keys. Softmax state is fp32 and online; the
-// 1/sqrt(d) scale and log2(e) fold into one FMA before v_exp_f32.
+// waves. At head width 64 the softmax's vector work per score is as large as
+// the matrix work, so the kernel moves what it can onto the matrix cores:
+//   * scores are computed transposed, S^T = K Q^T, so after the softmax every
+//     lane already holds the key slots the product O^T = V^T P^T wants as its
+//     B operand (no shuffles between the two products);
+//   * queries arrive pre-scaled by log2(e)/sqrt(d) (fused into the projection
+//     epilogue), and the score accumulator starts at -m (the running max), so
+//     p = exp2(S) needs no per-score arithmetic before v_exp_f32;
+//   * the softmax denominator is one more MFMA against a row of ones, so it
+//     sums exactly the bf16 P used in the numerator;
+//   * the running max only moves when a tile exceeds it by more than 8 (log2
+//     units); otherwise P may reach 2^8 and nothing is rescaled. Numerator
+//     and denominator share the reference, so the result is unchanged;
+//   * row maxima reduce across the four lanes of a query with the gfx950
+//     permlane swaps (VALU, not LDS).
+// V is kept transposed in HBM ([group][d][token]) so its A operand reads
+// contiguous keys.
 #pragma once
 
 #include "gqe_common.hpp"
@@ -36,25 +47,67 @@ struct AttnArgs {
     int32_t H;           // H0 + (Q1 != null)
     int32_t n_qt;        // query tiles per sequence
     int32_t o1_col;
-    float scale_log2;    // log2(e) / sqrt(d)
+    int32_t pad_;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
-    constexpr int BQ = 128, BKV = 64;
+// Tile shape: queries per wave, waves per workgroup, waves per SIMD the
+// register budget is sized for, keys per tile.
+#ifndef GQE_ATTN_QW
+#define GQE_ATTN_QW 32
+#endif
+#ifndef GQE_ATTN_NW
+#define GQE_ATTN_NW 8
+#endif
+#ifndef GQE_ATTN_WPE
+#define GQE_ATTN_WPE 2
+#endif
+#ifndef GQE_ATTN_BKV
+#define GQE_ATTN_BKV 128
+#endif
+constexpr int kAttnQW = GQE_ATTN_QW;
+constexpr int kAttnNW = GQE_ATTN_NW;
+constexpr int kAttnBKV = GQE_ATTN_BKV;
+constexpr float kLazyRescale = 8.f;   // log2 units the running max may lag by
+
+// Max over the four lanes {l16, l16+16, l16+32, l16+48} that hold one query.
+__device__ __forceinline__ float quad_row_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Byte offset of 16-byte chunk c of K row r (rows of KCH chunks, XOR swizzle).
+template <int KCH>
+__device__ __forceinline__ int k_chunk_off(int r, int c) {
+    return r * KCH * 16 + ((c ^ (r % KCH)) * 16);
+}
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQE_ATTN_WPE, GQE_ATTN_WPE)))
+void attn_fwd_kernel(AttnArgs a) {
+    constexpr int NT = NW * 64;
+    constexpr int QB = kAttnQW / 16;           // 16-query blocks per wave
+    constexpr int BQ = NW * kAttnQW;
+    constexpr int BKV = kAttnBKV;
+    constexpr int KB = BKV / 16;               // 16-key blocks per tile
+    constexpr int KC = BKV / 32;               // 32-key steps of the second product
     constexpr int ES = sizeof(T);
     constexpr int DK = D / 32;                 // 32-wide contraction steps over d
     constexpr int CB = D / 16;                 // 16-wide blocks of the output columns
-    constexpr int KP = D * ES + 16;            // LDS pitch of a K row (bytes)
-    constexpr int VP = BKV * ES + 16;          // LDS pitch of a V^T row (bytes)
+    // LDS layouts (both free of bank conflicts for the reads below, measured
+    // on gfx950): K rows are unpadded and their 16-byte chunks XOR-swizzled by
+    // the row index; V^T rows are padded to a pitch of 136 bytes (bf16), read
+    // as two 8-byte pieces.
+    constexpr int KCH = D * ES / 16;           // 16-byte chunks per K row
+    constexpr int KP = D * ES;                 // LDS pitch of a K row (bytes)
+    constexpr int VP = BKV * ES + (ES == 2 ? 8 : 16);   // LDS pitch of a V^T row (bytes)
     constexpr int K_BYTES = BKV * KP, V_BYTES = D * VP;
     constexpr int STAGE = K_BYTES + V_BYTES;
-    constexpr int KCH = D * ES / 16;           // 16-byte chunks per K row
     constexpr int VCH = BKV * ES / 16;         // 16-byte chunks per V^T row
-    constexpr int K_PER_T = BKV * KCH / 256;
-    constexpr int V_PER_T = D * VCH / 256;
+    constexpr int K_PER_T = (BKV * KCH + NT - 1) / NT;
+    constexpr int V_PER_T = (D * VCH + NT - 1) / NT;
     constexpr int VEC = 16 / ES;
-    static_assert(K_PER_T >= 1 && V_PER_T >= 1, "tile must cover 256 threads");
     __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -73,58 +126,92 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
     const T* Vg = (const T*)a.Vt + (int64_t)g * D * vrow + (int64_t)b * a.Tpad;
     const int64_t T_ = a.T;
     const int64_t tok0 = (int64_t)b * T_;
+    const int q_base = qt * BQ + wave * kAttnQW;     // first query of this wave
 
-    const int q_base = qt * BQ + wave * 32;     // first query of this wave
-    // Queries as the B operand of S^T = K Q^T: column l16 of block qb, d slice dk.
-    Frag<T> qf[2][DK];
+    // Queries (pre-scaled) as the B operand of S^T = K Q^T.
+    Frag<T> qf[QB][DK];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const int t = q_base + qb * 16 + l16;
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) {
             if (t < T_) {
                 qf[qb][dk] = ld_frag<T>(Qh + (tok0 + t) * qld + dk * 32 + 8 * q4);
             } else {
-                Frag<T> z;
                 if constexpr (ES == 2) {
-                    z.v = bf16x8{};
+                    qf[qb][dk].v = bf16x8{};
                 } else {
-                    z.lo = f32x4{0.f, 0.f, 0.f, 0.f};
-                    z.hi = z.lo;
+                    qf[qb][dk].lo = f32x4{0.f, 0.f, 0.f, 0.f};
+                    qf[qb][dk].hi = qf[qb][dk].lo;
                 }
-                qf[qb][dk] = z;
             }
         }
     }
-
-    f32x4 o[CB][2];
+    // A operand of the denominator product: row 0 of the block is all ones.
+    Frag<T> ones;
+    {
+        const float o1 = (l16 == 0) ? 1.f : 0.f;
+        if constexpr (ES == 2) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) o[cb][0] = o[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-    const float c = a.scale_log2;
+            for (int i = 0; i < 8; ++i) ones.v[i] = (bf16)o1;
+        } else {
+            ones.lo = f32x4{o1, o1, o1, o1};
+            ones.hi = ones.lo;
+        }
+    }
+
+    f32x4 o[CB][QB], lsum[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        lsum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Reference subtracted from the scores of each query (log2 units);
+    // -inf until the first tile sets it.
+    float mref[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mref[qb] = -INFINITY;
 
     const int q_hi = (int)min<int64_t>(T_, (int64_t)qt * BQ + BQ);   // queries of the tile are < q_hi
     const int n_kv = (q_hi - 1) / BKV + 1;
 
     u32x4 rk[K_PER_T], rv[V_PER_T];
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    constexpr bool K_EXACT = (BKV * KCH) % NT == 0, V_EXACT = (D * VCH) % NT == 0;
     auto gload = [&](int j) {
         const int s0 = j * BKV;
+        if (s0 + BKV <= T_ && K_EXACT && V_EXACT) {   // interior tile: no bounds to check
+#pragma unroll
+            for (int i = 0; i < K_PER_T; ++i) {
+                const int it = tid + NT * i;
+                rk[i] = ld16(Kg + (int64_t)(s0 + it / KCH) * D + (it % KCH) * VEC);
+            }
+#pragma unroll
+            for (int i = 0; i < V_PER_T; ++i) {
+                const int it = tid + NT * i;
+                rv[i] = ld16(Vg + (int64_t)(it / VCH) * vrow + s0 + (it % VCH) * VEC);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < K_PER_T; ++i) {
-            const int it = tid + 256 * i, r = it / KCH, ch = it % KCH;
-            rk[i] = (s0 + r < T_) ? ld16(Kg + (int64_t)(s0 + r) * D + ch * VEC) : zero;
+            const int it = tid + NT * i, r = it / KCH, ch = it % KCH;
+            rk[i] = (it < BKV * KCH && s0 + r < T_) ? ld16(Kg + (int64_t)(s0 + r) * D + ch * VEC) : zero;
         }
 #pragma unroll
         for (int i = 0; i < V_PER_T; ++i) {
-            const int it = tid + 256 * i, r = it / VCH, ch = it % VCH;
-            const int s = s0 + ch * VEC;       // first key of this chunk (in-bounds: Tpad pads)
-            u32x4 v = ld16(Vg + (int64_t)r * vrow + s);
-            if (s + VEC > T_) {                 // zero the keys at or beyond T
-                T* e = reinterpret_cast<T*>(&v);
+            const int it = tid + NT * i, r = it / VCH, ch = it % VCH;
+            const int s = s0 + ch * VEC;       // first key of this chunk (in bounds: Tpad pads)
+            u32x4 v = zero;
+            if (it < D * VCH) {
+                v = ld16(Vg + (int64_t)r * vrow + s);
+                if (s + VEC > T_) {             // zero the keys at or beyond T
+                    T* e = reinterpret_cast<T*>(&v);
 #pragma unroll
-                for (int q = 0; q < VEC; ++q)
-                    if (s + q >= T_) e[q] = from_f32<T>(0.f);
+                    for (int q = 0; q < VEC; ++q)
+                        if (s + q >= T_) e[q] = from_f32<T>(0.f);
+                }
             }
             rv[i] = v;
         }
@@ -134,13 +221,19 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
         char* Vs = Ks + K_BYTES;
 #pragma unroll
         for (int i = 0; i < K_PER_T; ++i) {
-            const int it = tid + 256 * i;
-            st16(Ks + (it / KCH) * KP + (it % KCH) * 16, rk[i]);
+            const int it = tid + NT * i;
+            if (K_EXACT || it < BKV * KCH) st16(Ks + k_chunk_off<KCH>(it / KCH, it % KCH), rk[i]);
         }
 #pragma unroll
         for (int i = 0; i < V_PER_T; ++i) {
-            const int it = tid + 256 * i;
-            st16(Vs + (it / VCH) * VP + (it % VCH) * 16, rv[i]);
+            const int it = tid + NT * i;
+            if (V_EXACT || it < D * VCH) {
+                // pitch VP is a multiple of 8 only: two 8-byte stores
+                typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+                char* p = Vs + (it / VCH) * VP + (it % VCH) * 16;
+                *reinterpret_cast<u32x2*>(p) = u32x2{rv[i][0], rv[i][1]};
+                *reinterpret_cast<u32x2*>(p + 8) = u32x2{rv[i][2], rv[i][3]};
+            }
         }
     };
 
@@ -150,25 +243,37 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
     for (int j = 0; j < n_kv; ++j) {
         if (j + 1 < n_kv) gload(j + 1);
         const int s0 = j * BKV;
-        if (s0 <= q_base + 31) {               // else every key is above every query of this wave
+        if (s0 <= q_base + kAttnQW - 1) {      // else every key is above every query of this wave
             const char* Ks = lds + (j & 1) * STAGE;
             const char* Vs = Ks + K_BYTES;
-            f32x4 s[4][2];
+            // S^T = K Q^T - m, accumulated from the current reference.
+            f32x4 s[KB][QB];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int qb = 0; qb < QB; ++qb) {
+                const float init = (mref[qb] == -INFINITY) ? 0.f : -mref[qb];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) s[kb][qb] = f32x4{init, init, init, init};
+            }
 #pragma unroll
             for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const Frag<T> kf = ld_frag<T>(Ks + (kb * 16 + l16) * KP + (dk * 32 + 8 * q4) * ES);
-                    s[kb][0] = mma16(kf, qf[0][dk], s[kb][0]);
-                    s[kb][1] = mma16(kf, qf[1][dk], s[kb][1]);
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int kr = kb * 16 + l16, kc0 = (dk * 32 + 8 * q4) * ES / 16;
+                    Frag<T> kf;
+                    if constexpr (ES == 2) {
+                        kf = ld_frag<T>(Ks + k_chunk_off<KCH>(kr, kc0));
+                    } else {   // 32 bytes = two swizzled chunks
+                        kf.lo = *reinterpret_cast<const f32x4*>(Ks + k_chunk_off<KCH>(kr, kc0));
+                        kf.hi = *reinterpret_cast<const f32x4*>(Ks + k_chunk_off<KCH>(kr, kc0 + 1));
+                    }
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16(kf, qf[qb][dk], s[kb][qb]);
                 }
             if (s0 + BKV - 1 > q_base) {       // a key may lie above a query: causal mask
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
+                    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
                             const int key = s0 + kb * 16 + 4 * q4 + v;
@@ -177,39 +282,38 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
                         }
             }
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < QB; ++qb) {
                 float mx = s[0][qb][0];
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][qb][v]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[qb], mx);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float corr = __builtin_amdgcn_exp2f((m_run[qb] - m_use) * c);
-                m_run[qb] = m_new;
-                const float nmc = -m_use * c;
-                float ls = 0.f;
+                mx = quad_row_max(mx);
+                // Move the reference only when needed: first tile, or scores
+                // more than kLazyRescale above it.
+                const bool need = (mref[qb] == -INFINITY && mx > -INFINITY) || mx > kLazyRescale;
+                if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                    const float delta = need ? mx : 0.f;
+                    const float corr = __builtin_amdgcn_exp2f(-delta);
+                    mref[qb] = need ? ((mref[qb] == -INFINITY) ? mx : mref[qb] + mx) : mref[qb];
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                    for (int kb = 0; kb < KB; ++kb) s[kb][qb] -= delta;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][v], c, nmc));
-                        s[kb][qb][v] = p;
-                        ls += p;
-                    }
-                l_run[qb] = l_run[qb] * corr + ls;
+                    for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= corr;
+                    lsum[qb] *= corr;
+                }
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= corr;
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) s[kb][qb][v] = __builtin_amdgcn_exp2f(s[kb][qb][v]);
             }
-            // O^T += V^T P^T, 32 keys per step: slot jj of lane group q4 is key
-            // 32*kc + 4*q4 + jj (jj < 4) or 32*kc + 16 + 4*q4 + (jj - 4).
+            // O^T += V^T P^T and l += 1^T P^T, 32 keys per step: slot jj of lane
+            // group q4 is key 32*kc + 4*q4 + jj (jj < 4) or 32*kc + 16 + 4*q4 + (jj - 4).
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                Frag<T> pf[2];
+            for (int kc = 0; kc < KC; ++kc) {
+                Frag<T> pf[QB];
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
+                for (int qb = 0; qb < QB; ++qb) {
                     if constexpr (ES == 2) {
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
@@ -220,6 +324,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
                         pf[qb].lo = s[2 * kc][qb];
                         pf[qb].hi = s[2 * kc + 1][qb];
                     }
+                    lsum[qb] = mma16(ones, pf[qb], lsum[qb]);
                 }
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
@@ -237,8 +342,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
                         vf.lo = *reinterpret_cast<const f32x4*>(vr + (32 * kc + 4 * q4) * ES);
                         vf.hi = *reinterpret_cast<const f32x4*>(vr + (32 * kc + 16 + 4 * q4) * ES);
                     }
-                    o[cb][0] = mma16(vf, pf[0], o[cb][0]);
-                    o[cb][1] = mma16(vf, pf[1], o[cb][1]);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) o[cb][qb] = mma16(vf, pf[qb], o[cb][qb]);
                 }
             }
         }
@@ -246,12 +351,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
         __syncthreads();
     }
 
-    // Normalise and store: lane holds query l16 of block qb, columns cb*16 + 4*q4 + v.
+    // Normalise and store. The denominator sits in row 0 of lsum (lanes of
+    // lane group 0, element 0); lane holds query l16 of block qb, columns
+    // cb*16 + 4*q4 + v.
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float l = l_run[qb];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l = __shfl(lsum[qb][0], l16);
         const float inv = 1.f / l;
         const int t = q_base + qb * 16 + l16;
         if (t >= T_) continue;

@@ -145,7 +145,7 @@ struct ProjSeg {
     int32_t col_begin;
     int32_t n_cols;
     int32_t mode;
-    int32_t pad_;
+    float scale;         // multiplies the fp32 result before rounding (queries: log2(e)/sqrt(d))
 };
 
 struct ProjArgs {
@@ -204,7 +204,9 @@ __global__ __launch_bounds__(256) void proj_gemm_kernel(ProjArgs a) {
             const ProjSeg& sg = a.seg[s];
             const int c = vc - sg.col_begin;
             if (c < 0 || c >= sg.n_cols || sg.mode == OUT_HEADS_T) continue;
-            const float* v = stage + r * Cfg::SP + cc;
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = stage[r * Cfg::SP + cc + q] * sg.scale;
             const int nv = min(8, sg.n_cols - c);
             if (sg.mode == OUT_ROWS_F32) {
                 float* o = (float*)sg.out + row * sg.ld_out + c;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void proj_gemm_kernel(ProjArgs a) {
             T* o = (T*)sg.out + ((int64_t)(c / a.d) * a.d + (c % a.d)) * (a.Bt * a.Tpad) + b * a.Tpad + t;
             float v[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = stage[(rr + q) * Cfg::SP + cl];
+            for (int q = 0; q < 8; ++q) v[q] = stage[(rr + q) * Cfg::SP + cl] * sg.scale;
             if (row + 8 <= a.M_rows && t + 8 <= a.T && (t % 8) == 0) {
                 store8<T>(o, v);
             } else {
@@ -273,6 +275,7 @@ struct GroupArgs {
     int32_t d;
     int32_t E;
     int32_t nC;
+    float scale;              // multiplies the fp32 result before rounding
 };
 
 template <typename T, class Cfg>
@@ -308,7 +311,10 @@ __global__ __launch_bounds__(256) void grouped_q_kernel(GroupArgs a) {
             const int r = it / CCH, cc = (it % CCH) * 8;
             const int drow = s_dst[r];
             if (drow < 0 || cc >= a.d) continue;
-            store8<T>((T*)a.Qr + (int64_t)drow * a.d + cc, stage + r * Cfg::SP + cc);
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = stage[r * Cfg::SP + cc + q] * a.scale;
+            store8<T>((T*)a.Qr + (int64_t)drow * a.d + cc, v);
         }
         __syncthreads();  // the stage and s_dst are reused by the next row tile
     }

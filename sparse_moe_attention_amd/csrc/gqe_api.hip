@@ -33,8 +33,9 @@ using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
 using GrpBf16 = TileCfg<bf16, 128, 64, 4, 1>;
 using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
 
-constexpr int kBQ = 128;   // attention query tile
-constexpr int kKVPad = 64; // sequence padding of the K / V^T buffers
+constexpr int kAttnWaves = kAttnNW;             // waves per attention workgroup
+constexpr int kBQ = kAttnWaves * kAttnQW;       // attention query tile
+constexpr int kKVPad = kAttnBKV;  // sequence padding of the K / V^T buffers: whole key tiles
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -112,7 +113,8 @@ void launch_proj(ProjArgs& a, int total_cols, hipStream_t st) {
 struct SegList {
     ProjArgs a;
     int cols = 0;
-    void add(const void* W, int n_cols, void* out, int mode, int64_t ld_out, const float* bias) {
+    void add(const void* W, int n_cols, void* out, int mode, int64_t ld_out, const float* bias,
+             float scale = 1.f) {
         ProjSeg& s = a.seg[a.n_segs++];
         s.W = W;
         s.out = out;
@@ -121,7 +123,7 @@ struct SegList {
         s.col_begin = cols;
         s.n_cols = n_cols;
         s.mode = mode;
-        s.pad_ = 0;
+        s.scale = scale;
         cols += (int)align_up((size_t)n_cols, 8);
     }
 };
@@ -145,11 +147,16 @@ void run_proj(const Dims& d, SegList& sl, hipStream_t st) {
     else launch_proj<bf16, ProjBf16>(sl.a, sl.cols, st);
 }
 
+// Queries are stored pre-multiplied by log2(e)/sqrt(d): the attention kernel
+// then works in log2 units with no per-score scaling.
+float q_scale(const Dims& d) { return (float)(1.4426950408889634 / std::sqrt((double)d.d)); }
+
 void run_grouped_q(const Dims& d, const void* x, const void* Wq, void* Qr, const int32_t* perm,
                    const int32_t* dst, const int32_t* cbase, hipStream_t st) {
     GroupArgs g;
     g.X = x; g.Wq = Wq; g.Qr = Qr; g.perm = perm; g.dst = dst; g.cbase = cbase;
     g.ldx = d.D; g.K = (int)d.D; g.d = d.d; g.E = d.E; g.nC = (int)d.nC;
+    g.scale = q_scale(d);
     const dim3 grid((unsigned)(d.nC * d.E));
     if (d.f32) hipLaunchKernelGGL((grouped_q_kernel<float, GrpF32>), grid, dim3(256), 0, st, g);
     else hipLaunchKernelGGL((grouped_q_kernel<bf16, GrpBf16>), grid, dim3(256), 0, st, g);
@@ -160,14 +167,13 @@ void run_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
     a.Tpad = d.Tpad;
     a.Bt = (int)d.B;
     a.n_qt = (int)((d.T + kBQ - 1) / kBQ);
-    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
-    const dim3 grid((unsigned)((int64_t)a.H * d.B * a.n_qt));
+    const dim3 grid((unsigned)((int64_t)a.H * d.B * a.n_qt)), block(kAttnWaves * 64);
     if (d.f32) {
-        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((attn_fwd_kernel<float, 32>), grid, dim3(256), 0, st, a);
+        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64, kAttnWaves>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_fwd_kernel<float, 32, kAttnWaves>), grid, block, 0, st, a);
     } else {
-        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((attn_fwd_kernel<bf16, 32>), grid, dim3(256), 0, st, a);
+        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64, kAttnWaves>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_fwd_kernel<bf16, 32, kAttnWaves>), grid, block, 0, st, a);
     }
 }
 
@@ -201,7 +207,7 @@ gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* 
         SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
         sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
         sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
-        sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr);
+        sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
         run_proj(d, sl, st);
     }
     int32_t* cbase = (int32_t*)at(ws, L.cbase);
@@ -321,7 +327,7 @@ gqe_status gqe_attn_fwd_timed(const gqe_shape* s, const void* x, const void* Wr,
     SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
     sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
     sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
-    sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr);
+    sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
     sl.add(Wr, d.E, lg, OUT_ROWS_F32, d.E, br);
     run_proj(d, sl, st);
     mk.at(1);
@@ -393,7 +399,7 @@ gqe_status gqa_attn_fwd_timed(int64_t B, int64_t T, int64_t D, int32_t Hq, int32
     SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
     sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
     sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
-    sl.add(Wq, Hq * d.d, at(ws, L.Q), OUT_ROWS, qld, nullptr);
+    sl.add(Wq, Hq * d.d, at(ws, L.Q), OUT_ROWS, qld, nullptr, q_scale(d));
     run_proj(d, sl, st);
     AttnArgs a;
     std::memset(&a, 0, sizeof(a));
