@@ -261,13 +261,15 @@ def _rows_attention(x, heads, Wk, Wv, G, d, B, T, rows, kv_chunk):
                 if ts[i] < c0:
                     continue
                 hi = min(c1, int(ts[i]) + 1) - c0
-                s = np.einsum("hd,shd->hs", qv[i], Kc[:hi, grp]) * scale   # [H,hi]
-                m_new = np.maximum(m[i], s.max(axis=1))
-                corr = np.exp(m[i] - m_new)
-                e = np.exp(s - m_new[:, None])
-                l[i] = l[i] * corr + e.sum(axis=1)
-                acc[i] = acc[i] * corr[:, None] + np.einsum("hs,shd->hd", e, Vc[:hi, grp])
-                m[i] = m_new
+                for hh in range(H):
+                    g = grp[hh]
+                    s = (Kc[:hi, g] @ qv[i, hh]) * scale            # [hi]
+                    m_new = max(m[i, hh], s.max())
+                    corr = np.exp(m[i, hh] - m_new)
+                    e = np.exp(s - m_new)
+                    l[i, hh] = l[i, hh] * corr + e.sum()
+                    acc[i, hh] = acc[i, hh] * corr + e @ Vc[:hi, g]
+                    m[i, hh] = m_new
     return acc / l[:, :, None]
 
 
