@@ -7,9 +7,11 @@
 // GQA baseline runs one per query head. Both are the same kernel: a head is a
 // query source (base, row stride), a KV group and an output column.
 //
-// Work split: one workgroup = one head, one sequence, NW waves x QW queries.
-// K/V tiles of 64 keys are staged in double-buffered LDS and shared by the
-// waves. At head width 64 the softmax's vector work per score is as large as
+// Work split: one workgroup = one KV group, one sequence, NW waves x QW query
+// rows, where the rows are all query heads reading that group (for GQE: the
+// group's k routed experts, plus the shared head on its group), token by
+// token. K/V tiles are staged in double-buffered LDS once and serve every
+// head of the group. At head width 64 the softmax's vector work per score is as large as
 // the matrix work, so the kernel moves what it can onto the matrix cores:
 //   * scores are computed transposed, S^T = K Q^T, so after the softmax every
 //     lane already holds the key slots the product O^T = V^T P^T wants as its
@@ -33,21 +35,20 @@
 namespace gqe {
 
 struct AttnArgs {
-    const void* Q0;      // main heads: query of token n, head h at Q0 + n*q0_ld + h*d
+    const void* Q0;      // main heads: query of token n, main head j at Q0 + n*q0_ld + j*d
     const void* Q1;      // extra (shared) head: Q1 + n*q1_ld, or null
     const void* K;       // [G][Bt][Tpad][d]
     const void* Vt;      // [G][d][Bt*Tpad]
-    void* O;             // main head h -> O + n*o_ld + h*d; extra head -> O + n*o_ld + o1_col
+    void* O;             // main head j -> O + n*o_ld + j*d; extra head -> O + n*o_ld + o1_col
     int64_t q0_ld, q1_ld, o_ld;
     int64_t T, Tpad;
     int32_t Bt;
-    int32_t H0;          // number of main heads
-    int32_t kv_div;      // main head h reads KV group h / kv_div
-    int32_t kv1;         // KV group of the extra head
-    int32_t H;           // H0 + (Q1 != null)
-    int32_t n_qt;        // query tiles per sequence
+    int32_t G;           // KV groups
+    int32_t R;           // main heads per group: main head j = g*R + r reads group g
+    int32_t kv1;         // the group whose rows also carry the extra head (if Q1)
+    int32_t n_o;         // row tiles per sequence of a regular group (R rows per token)
+    int32_t n_x;         // row tiles per sequence of group kv1 when it carries the extra head
     int32_t o1_col;
-    int32_t pad_;
 };
 
 // Tile shape: queries per wave, waves per workgroup, waves per SIMD the
@@ -112,31 +113,73 @@ void attn_fwd_kernel(AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int hb = a.H * a.Bt;
-    const int qt = a.n_qt - 1 - (int)(blockIdx.x / hb);     // longest rows first
-    const int rem = (int)(blockIdx.x % hb);
-    const int h = rem / a.Bt, b = rem % a.Bt;
-    const bool extra = h >= a.H0;
-    const int g = extra ? a.kv1 : h / a.kv_div;
-    const T* Qh = extra ? (const T*)a.Q1 : (const T*)a.Q0 + (int64_t)h * D;
-    const int64_t qld = extra ? a.q1_ld : a.q0_ld;
-    T* Oh = (T*)a.O + (extra ? (int64_t)a.o1_col : (int64_t)h * D);
+    // Work unit: one KV group of one sequence and one tile of BQ query rows.
+    // A group's rows are its R main heads token by token (row = t*Rg + r),
+    // plus the extra head for group kv1, so one staged K/V tile serves every
+    // query head that reads this group. Groups thus come in two classes:
+    // regular (R rows per token, n_o tiles) and the extra group (R+1 rows per
+    // token, n_x tiles). Workgroups are ordered by level, longest rows first:
+    // level l holds tile n_o-1-l of every regular group and the extra group's
+    // tiles that end at about the same token, [n_x - e(l+1), n_x - e(l)) with
+    // e(l) = l*n_x/n_o; count(l) workgroups precede level l.
+    const bool xcls = a.Q1 != nullptr;
+    const int n_reg = xcls ? a.G - 1 : a.G;                // regular groups
+    const int64_t nrb = (int64_t)a.Bt * n_reg;              // regular workgroups per level
+    auto count = [&](int l) -> int64_t {
+        return nrb * l + (xcls ? (int64_t)a.Bt * ((int64_t)l * a.n_x / a.n_o) : 0);
+    };
+    const int64_t L = blockIdx.x;
+    int lv = (int)((double)L / ((double)nrb + (xcls ? (double)a.Bt * a.n_x / a.n_o : 0.0)));
+    lv = min(max(lv, 0), a.n_o - 1);
+    while (lv > 0 && count(lv) > L) --lv;
+    while (lv + 1 < a.n_o && count(lv + 1) <= L) ++lv;
+    const int64_t pos = L - count(lv);
+    int g, b, qt, Rg;
+    if (pos < nrb) {
+        const int gi = (int)(pos / a.Bt);
+        b = (int)(pos % a.Bt);
+        g = (xcls && gi >= a.kv1) ? gi + 1 : gi;
+        qt = a.n_o - 1 - lv;
+        Rg = a.R;
+    } else {
+        const int64_t q = pos - nrb;
+        b = (int)(q % a.Bt);
+        g = a.kv1;
+        qt = a.n_x - 1 - (int)((int64_t)lv * a.n_x / a.n_o) - (int)(q / a.Bt);
+        Rg = a.R + 1;
+    }
+    const int64_t T_ = a.T;
+    const int64_t n_rows = T_ * Rg;
     const T* Kg = (const T*)a.K + ((int64_t)g * a.Bt + b) * a.Tpad * D;
     const int64_t vrow = (int64_t)a.Bt * a.Tpad;
     const T* Vg = (const T*)a.Vt + (int64_t)g * D * vrow + (int64_t)b * a.Tpad;
-    const int64_t T_ = a.T;
     const int64_t tok0 = (int64_t)b * T_;
-    const int q_base = qt * BQ + wave * kAttnQW;     // first query of this wave
+    const int row0 = qt * BQ + wave * kAttnQW;           // first row of this wave
+    // Token of each row this lane holds (query column l16 of block qb).
+    int tq[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) tq[qb] = (row0 + qb * 16 + l16) / Rg;
+    const int t_first = row0 / Rg;                       // tokens spanned by this wave
+    const int t_last = (int)min<int64_t>(T_ - 1, (row0 + kAttnQW - 1) / Rg);
+    // Query and output row pointers of a row (token t, head slot r).
+    auto q_row = [&](int t, int r) -> const T* {
+        return r < a.R ? (const T*)a.Q0 + (tok0 + t) * a.q0_ld + (int64_t)(g * a.R + r) * D
+                       : (const T*)a.Q1 + (tok0 + t) * a.q1_ld;
+    };
+    auto o_row = [&](int t, int r) -> T* {
+        return (T*)a.O + (tok0 + t) * a.o_ld + (r < a.R ? (int64_t)(g * a.R + r) * D : (int64_t)a.o1_col);
+    };
 
     // Queries (pre-scaled) as the B operand of S^T = K Q^T.
     Frag<T> qf[QB][DK];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int t = q_base + qb * 16 + l16;
+        const int rho = row0 + qb * 16 + l16;
+        const T* qp = (rho < n_rows) ? q_row(tq[qb], rho % Rg) : nullptr;
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) {
-            if (t < T_) {
-                qf[qb][dk] = ld_frag<T>(Qh + (tok0 + t) * qld + dk * 32 + 8 * q4);
+            if (qp != nullptr) {
+                qf[qb][dk] = ld_frag<T>(qp + dk * 32 + 8 * q4);
             } else {
                 if constexpr (ES == 2) {
                     qf[qb][dk].v = bf16x8{};
@@ -173,8 +216,9 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mref[qb] = -INFINITY;
 
-    const int q_hi = (int)min<int64_t>(T_, (int64_t)qt * BQ + BQ);   // queries of the tile are < q_hi
-    const int n_kv = (q_hi - 1) / BKV + 1;
+    // Keys up to the last token of the tile.
+    const int t_hi = (int)min<int64_t>(T_ - 1, ((int64_t)qt * BQ + BQ - 1) / Rg);
+    const int n_kv = t_hi / BKV + 1;
 
     u32x4 rk[K_PER_T], rv[V_PER_T];
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -243,7 +287,7 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int j = 0; j < n_kv; ++j) {
         if (j + 1 < n_kv) gload(j + 1);
         const int s0 = j * BKV;
-        if (s0 <= q_base + kAttnQW - 1) {      // else every key is above every query of this wave
+        if (s0 <= t_last) {                    // else every key is above every query of this wave
             const char* Ks = lds + (j & 1) * STAGE;
             const char* Vs = Ks + K_BYTES;
             // S^T = K Q^T - m, accumulated from the current reference.
@@ -269,7 +313,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16(kf, qf[qb][dk], s[kb][qb]);
                 }
-            if (s0 + BKV - 1 > q_base) {       // a key may lie above a query: causal mask
+            if (s0 + BKV - 1 > t_first) {      // a key may lie above a query: causal mask
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -277,8 +321,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
                             const int key = s0 + kb * 16 + 4 * q4 + v;
-                            const int qry = q_base + qb * 16 + l16;
-                            if (key > qry) s[kb][qb][v] = -INFINITY;
+                            if (key > tq[qb]) s[kb][qb][v] = -INFINITY;
                         }
             }
 #pragma unroll
@@ -358,9 +401,9 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
         const float l = __shfl(lsum[qb][0], l16);
         const float inv = 1.f / l;
-        const int t = q_base + qb * 16 + l16;
-        if (t >= T_) continue;
-        T* orow = Oh + (tok0 + t) * a.o_ld;
+        const int rho = row0 + qb * 16 + l16;
+        if (rho >= n_rows) continue;
+        T* orow = o_row(tq[qb], rho % Rg);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             T* op = orow + cb * 16 + 4 * q4;

@@ -166,8 +166,12 @@ void run_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
     a.T = d.T;
     a.Tpad = d.Tpad;
     a.Bt = (int)d.B;
-    a.n_qt = (int)((d.T + kBQ - 1) / kBQ);
-    const dim3 grid((unsigned)((int64_t)a.H * d.B * a.n_qt)), block(kAttnWaves * 64);
+    const bool xcls = a.Q1 != nullptr;
+    a.n_o = (int)((d.T * a.R + kBQ - 1) / kBQ);
+    a.n_x = xcls ? (int)((d.T * (a.R + 1) + kBQ - 1) / kBQ) : 0;
+    a.G = d.G;
+    const int64_t n_wg = d.B * ((int64_t)(xcls ? d.G - 1 : d.G) * a.n_o + a.n_x);
+    const dim3 grid((unsigned)n_wg), block(kAttnWaves * 64);
     if (d.f32) {
         if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64, kAttnWaves>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((attn_fwd_kernel<float, 32, kAttnWaves>), grid, block, 0, st, a);
@@ -230,10 +234,8 @@ gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* 
     a.Vt = at(ws, L.Vt);
     a.O = C;
     a.o_ld = (int64_t)(d.GK + 2) * d.d;
-    a.H0 = d.GK;
-    a.kv_div = d.k;
+    a.R = d.k;                 // routed head j = g*k + r: hard slot j of C
     a.kv1 = d.s0;
-    a.H = d.GK + 1;
     a.o1_col = (d.GK + 1) * d.d;
     mk.at(5);
     run_attention(d, a, st);
@@ -410,10 +412,8 @@ gqe_status gqa_attn_fwd_timed(int64_t B, int64_t T, int64_t D, int32_t Hq, int32
     a.Vt = at(ws, L.Vt);
     a.O = at(ws, L.C);
     a.o_ld = qld;
-    a.H0 = Hq;
-    a.kv_div = Hq / G;
+    a.R = Hq / G;              // head h reads group h / (Hq/G)
     a.kv1 = 0;
-    a.H = Hq;
     mk.at(1);
     run_attention(d, a, st);
     mk.at(2);
