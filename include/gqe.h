@@ -114,9 +114,11 @@ gqe_status gqe_route(const gqe_shape* s, const void* x, const void* Wr, const fl
  *   Wq_sh   [d_h, D]              query projection of the shared head
  *   Wo      [D, (G*k+2)*d_h]      output projection over the merged slots
  *   idx     [B*T, G, k] int32     picked experts, each in [0, M), distinct
- *                                 within a group; an entry outside [0, M) is
- *                                 skipped and its hard slot holds unspecified
- *                                 values (no out-of-bounds access results)
+ *                                 within a group; an entry outside [0, M), or
+ *                                 repeating an earlier rank's expert in its
+ *                                 group, is skipped and its hard slot holds
+ *                                 unspecified values (no out-of-bounds access
+ *                                 results)
  *   w       [B*T, G, k] fp32      weights of the weighted slot
  *   out     [B*T, D]              out: layer output
  *   slots_out [B*T, (G*k+2)*d_h]  out (NULL to skip): the merged slots */

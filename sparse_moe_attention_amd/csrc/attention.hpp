@@ -111,7 +111,10 @@ void attn_fwd_kernel(AttnArgs a) {
     constexpr int VEC = 16 / ES;
     __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The wave index is uniform across the wave; saying so keeps everything
+    // derived from it (row ranges, skip and mask tests) in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
     // Work unit: one KV group of one sequence and one tile of BQ query rows.
     // A group's rows are its R main heads token by token (row = t*Rg + r),
@@ -291,12 +294,12 @@ void attn_fwd_kernel(AttnArgs a) {
             const char* Ks = lds + (j & 1) * STAGE;
             const char* Vs = Ks + K_BYTES;
             // S^T = K Q^T - m, accumulated from the current reference.
-            f32x4 s[KB][QB];
+            // The first MFMA of every block takes -m as its C operand.
+            f32x4 s[KB][QB], init[QB];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const float init = (mref[qb] == -INFINITY) ? 0.f : -mref[qb];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) s[kb][qb] = f32x4{init, init, init, init};
+                const float m0 = (mref[qb] == -INFINITY) ? 0.f : -mref[qb];
+                init[qb] = f32x4{m0, m0, m0, m0};
             }
 #pragma unroll
             for (int dk = 0; dk < DK; ++dk)
@@ -311,7 +314,7 @@ void attn_fwd_kernel(AttnArgs a) {
                         kf.hi = *reinterpret_cast<const f32x4*>(Ks + k_chunk_off<KCH>(kr, kc0 + 1));
                     }
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16(kf, qf[qb][dk], s[kb][qb]);
+                    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16(kf, qf[qb][dk], dk == 0 ? init[qb] : s[kb][qb]);
                 }
             if (s0 + BKV - 1 > t_first) {      // a key may lie above a query: causal mask
 #pragma unroll

@@ -25,7 +25,8 @@ namespace gqe {
 constexpr int kChunk = 256;   // tokens per routing chunk (= workgroup size)
 
 // MODE 0: route from fp32 logits [N, G*M] -> idx, w and the histogram.
-// MODE 1: histogram of a caller-given idx (entries outside [0, M) skipped).
+// MODE 1: histogram of a caller-given idx (entries outside [0, M), and repeats
+// of an earlier rank's expert in the same group, are skipped).
 template <int MODE>
 __global__ __launch_bounds__(256) void route_kernel(const float* logits, int32_t* idx, float* w,
                                                     int32_t* hist, int64_t N, int G, int M, int k) {
@@ -73,7 +74,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* logits, int32_t
             for (int g = 0; g < G; ++g)
                 for (int r = 0; r < k; ++r) {
                     const int m = irow[g * k + r];
-                    if (m >= 0 && m < M) atomicAdd(&h_lds[g * M + m], 1);
+                    bool first = m >= 0 && m < M;          // out-of-range picks are skipped
+                    for (int q = 0; q < r && first; ++q) first = irow[g * k + q] != m;   // so are repeats
+                    if (first) atomicAdd(&h_lds[g * M + m], 1);
                 }
         }
     }
@@ -131,27 +134,47 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* hist, int32_t
     if (t < E) cbase[(int64_t)nC * E + t] = off[t] + tot[t];
 }
 
-// Workgroup = chunk, thread = expert. Lists the picks of expert e in chunk c
-// in token order: perm = token, dst = row of the dense [N, G, k] layout.
+// Workgroup = chunk of 256 tokens, thread = token. For every expert e the
+// picks of the chunk are listed in token order at [cbase[c][e], ...): a
+// token's rank is the number of earlier tokens of its wave that picked e
+// (wave ballot) plus the totals of the earlier waves (one LDS exchange).
+// perm = token, dst = row of the dense [N, G, k] layout (the first rank r at
+// which the token picked e). Two passes over the experts: count, then write.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* idx, const int32_t* cbase, int32_t* perm,
                                                       int32_t* dst, int64_t N, int G, int M, int k) {
+    __shared__ int32_t wtot[4][256];           // picks of expert e in each wave of the chunk
     const int E = G * M;
-    const int e = threadIdx.x;
-    if (e >= E) return;
-    const int g = e / M, m = e % M;
-    int pos = cbase[(int64_t)blockIdx.x * E + e];
-    const int64_t n0 = (int64_t)blockIdx.x * kChunk;
-    const int64_t n1 = min<int64_t>(N, n0 + kChunk);
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int64_t n = (int64_t)blockIdx.x * kChunk + tid;
+    const bool valid = n < N;
     const int GK = G * k;
-    for (int64_t n = n0; n < n1; ++n) {
-        const int32_t* row = idx + n * GK + g * k;
-        for (int r = 0; r < k; ++r)
-            if (row[r] == m) {
-                perm[pos] = (int32_t)n;
-                dst[pos] = (int32_t)(n * GK + g * k + r);
-                ++pos;
-            }
-    }
+    const int32_t* row = idx + (valid ? n : 0) * GK;
+    // r at which this token picked expert m of group g, or -1.
+    auto pick_rank = [&](int g, int m) {
+        int hit = -1;
+        if (valid)
+            for (int r = k - 1; r >= 0; --r)
+                if (row[g * k + r] == m) hit = r;
+        return hit;
+    };
+    for (int g = 0; g < G; ++g)
+        for (int m = 0; m < M; ++m) {
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(pick_rank(g, m) >= 0);
+            if ((tid & 63) == 0) wtot[wave][g * M + m] = __builtin_popcountll(mask);
+        }
+    __syncthreads();
+    for (int g = 0; g < G; ++g)
+        for (int m = 0; m < M; ++m) {
+            const int r = pick_rank(g, m);
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(r >= 0);
+            if (r < 0) continue;
+            const int e = g * M + m;
+            int pos = cbase[(int64_t)blockIdx.x * E + e];
+            for (int w = 0; w < wave; ++w) pos += wtot[w][e];
+            pos += __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+            perm[pos] = (int32_t)n;
+            dst[pos] = (int32_t)(n * GK + g * k + r);
+        }
 }
 
 // Weighted slot: C[n, GK*d + c] = sum_s w[n, s] * C[n, s*d + c] over the GK
