@@ -78,10 +78,24 @@ __device__ __forceinline__ float quad_row_max(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Byte offset of 16-byte chunk c of K row r (rows of KCH chunks, XOR swizzle).
+// Key held by row i of 16-row score block kb. The order makes the eight P
+// values a lane holds for one 32-key step eight consecutive keys, so each V^T
+// fragment of the second product is one 16-byte LDS read.
+__device__ __forceinline__ int key_of_row(int kb, int i) {
+    return 32 * (kb >> 1) + 8 * (i >> 2) + 4 * (kb & 1) + (i & 3);
+}
+// LDS layouts, both measured free of bank conflicts on gfx950 for the reads
+// below. K: rows of KCH 16-byte chunks, chunk c of row r at c ^ swz(r), where
+// swz spreads the rows key_of_row visits for one block. V^T: rows of VCH
+// chunks, chunk c of row r at c ^ (r % VCH).
 template <int KCH>
 __device__ __forceinline__ int k_chunk_off(int r, int c) {
-    return r * KCH * 16 + ((c ^ (r % KCH)) * 16);
+    const int swz = ((r & 3) | (((r >> 3) & 1) << 2)) & (KCH - 1);
+    return r * KCH * 16 + ((c ^ swz) * 16);
+}
+template <int VCH>
+__device__ __forceinline__ int v_chunk_off(int r, int c) {
+    return r * VCH * 16 + ((c ^ (r & (VCH - 1))) * 16);
 }
 
 template <typename T, int D, int NW>
@@ -96,16 +110,10 @@ void attn_fwd_kernel(AttnArgs a) {
     constexpr int ES = sizeof(T);
     constexpr int DK = D / 32;                 // 32-wide contraction steps over d
     constexpr int CB = D / 16;                 // 16-wide blocks of the output columns
-    // LDS layouts (both free of bank conflicts for the reads below, measured
-    // on gfx950): K rows are unpadded and their 16-byte chunks XOR-swizzled by
-    // the row index; V^T rows are padded to a pitch of 136 bytes (bf16), read
-    // as two 8-byte pieces.
     constexpr int KCH = D * ES / 16;           // 16-byte chunks per K row
-    constexpr int KP = D * ES;                 // LDS pitch of a K row (bytes)
-    constexpr int VP = BKV * ES + (ES == 2 ? 8 : 16);   // LDS pitch of a V^T row (bytes)
-    constexpr int K_BYTES = BKV * KP, V_BYTES = D * VP;
-    constexpr int STAGE = K_BYTES + V_BYTES;
     constexpr int VCH = BKV * ES / 16;         // 16-byte chunks per V^T row
+    constexpr int K_BYTES = BKV * KCH * 16, V_BYTES = D * VCH * 16;
+    constexpr int STAGE = K_BYTES + V_BYTES;
     constexpr int K_PER_T = (BKV * KCH + NT - 1) / NT;
     constexpr int V_PER_T = (D * VCH + NT - 1) / NT;
     constexpr int VEC = 16 / ES;
@@ -274,13 +282,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < V_PER_T; ++i) {
             const int it = tid + NT * i;
-            if (V_EXACT || it < D * VCH) {
-                // pitch VP is a multiple of 8 only: two 8-byte stores
-                typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
-                char* p = Vs + (it / VCH) * VP + (it % VCH) * 16;
-                *reinterpret_cast<u32x2*>(p) = u32x2{rv[i][0], rv[i][1]};
-                *reinterpret_cast<u32x2*>(p + 8) = u32x2{rv[i][2], rv[i][3]};
-            }
+            if (V_EXACT || it < D * VCH) st16(Vs + v_chunk_off<VCH>(it / VCH, it % VCH), rv[i]);
         }
     };
 
@@ -305,7 +307,7 @@ void attn_fwd_kernel(AttnArgs a) {
             for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    const int kr = kb * 16 + l16, kc0 = (dk * 32 + 8 * q4) * ES / 16;
+                    const int kr = key_of_row(kb, l16), kc0 = (dk * 32 + 8 * q4) * ES / 16;
                     Frag<T> kf;
                     if constexpr (ES == 2) {
                         kf = ld_frag<T>(Ks + k_chunk_off<KCH>(kr, kc0));
@@ -323,7 +325,7 @@ void attn_fwd_kernel(AttnArgs a) {
                     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            const int key = s0 + kb * 16 + 4 * q4 + v;
+                            const int key = s0 + key_of_row(kb, 4 * q4 + v);
                             if (key > tq[qb]) s[kb][qb][v] = -INFINITY;
                         }
             }
@@ -354,7 +356,7 @@ void attn_fwd_kernel(AttnArgs a) {
                     for (int v = 0; v < 4; ++v) s[kb][qb][v] = __builtin_amdgcn_exp2f(s[kb][qb][v]);
             }
             // O^T += V^T P^T and l += 1^T P^T, 32 keys per step: slot jj of lane
-            // group q4 is key 32*kc + 4*q4 + jj (jj < 4) or 32*kc + 16 + 4*q4 + (jj - 4).
+            // group q4 is key 32*kc + 8*q4 + jj (blocks 2kc and 2kc+1, see key_of_row).
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 Frag<T> pf[QB];
@@ -374,19 +376,14 @@ void attn_fwd_kernel(AttnArgs a) {
                 }
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
-                    const char* vr = Vs + (cb * 16 + l16) * VP;
+                    // Keys 32*kc + 8*q4 .. +7 of V^T row cb*16 + l16.
+                    const int vr = cb * 16 + l16, vc = (32 * kc + 8 * q4) * ES / 16;
                     Frag<T> vf;
                     if constexpr (ES == 2) {
-                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + (32 * kc + 4 * q4) * ES);
-                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + (32 * kc + 16 + 4 * q4) * ES);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            vf.v[v] = lo[v];
-                            vf.v[4 + v] = hi[v];
-                        }
+                        vf = ld_frag<T>(Vs + v_chunk_off<VCH>(vr, vc));
                     } else {
-                        vf.lo = *reinterpret_cast<const f32x4*>(vr + (32 * kc + 4 * q4) * ES);
-                        vf.hi = *reinterpret_cast<const f32x4*>(vr + (32 * kc + 16 + 4 * q4) * ES);
+                        vf.lo = *reinterpret_cast<const f32x4*>(Vs + v_chunk_off<VCH>(vr, vc));
+                        vf.hi = *reinterpret_cast<const f32x4*>(Vs + v_chunk_off<VCH>(vr, vc + 1));
                     }
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) o[cb][qb] = mma16(vf, pf[qb], o[cb][qb]);

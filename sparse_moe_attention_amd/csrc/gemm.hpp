@@ -16,7 +16,24 @@
 
 namespace gqe {
 
-constexpr int kPitch = 144;  // bytes per LDS row: 128 bytes of data + 16 of padding
+// LDS tile rows are 128 bytes (one K step), unpadded; the eight 16-byte
+// chunks of row r are stored XOR-swizzled by r % 8, which keeps both the
+// row-wise stores and the 16-lanes-down-a-column fragment reads free of bank
+// conflicts on gfx950 (a 144-byte padded pitch measured 2-way conflicts).
+constexpr int kPitch = 128;
+__device__ __forceinline__ int tile_off(int r, int c) { return r * kPitch + ((c ^ (r & 7)) << 4); }
+
+// Eight contraction elements of row r starting at chunk c (two chunks for fp32).
+template <typename T> __device__ __forceinline__ Frag<T> ld_tile_frag(const char* base, int r, int c);
+template <> __device__ __forceinline__ Frag<bf16> ld_tile_frag<bf16>(const char* base, int r, int c) {
+    return ld_frag<bf16>(base + tile_off(r, c));
+}
+template <> __device__ __forceinline__ Frag<float> ld_tile_frag<float>(const char* base, int r, int c) {
+    Frag<float> f;
+    f.lo = *reinterpret_cast<const f32x4*>(base + tile_off(r, c));
+    f.hi = *reinterpret_cast<const f32x4*>(base + tile_off(r, c + 1));
+    return f;
+}
 
 template <typename T, int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
@@ -39,17 +56,21 @@ struct TileCfg {
 
 // K loop. a_row[i] / b_row[i] point at the tile rows this thread loads
 // (row tid/8 + 32*i), already offset by its 16-byte column chunk; nullptr
-// rows read as zeros, as do columns at or beyond K. Leaves the C block of
-// this wave in acc and the LDS free (all waves past the final barrier).
+// rows read as zeros, as do columns at or beyond K. Global loads run two K
+// steps ahead of the MFMAs (two register sets), LDS holds two steps. Leaves
+// the C block of this wave in acc and the LDS free (all waves past the final
+// barrier).
 template <typename T, class Cfg>
 __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)[Cfg::A_PER_THREAD],
                                               const T* const (&b_row)[Cfg::B_PER_THREAD], int K,
                                               f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int c16 = tid & 7;
     const int nk = (K + Cfg::BK - 1) / Cfg::BK;
-    u32x4 ra[Cfg::A_PER_THREAD], rb[Cfg::B_PER_THREAD];
+    u32x4 ra0[Cfg::A_PER_THREAD], rb0[Cfg::B_PER_THREAD];
+    u32x4 ra1[Cfg::A_PER_THREAD], rb1[Cfg::B_PER_THREAD];
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
 #pragma unroll
@@ -57,7 +78,7 @@ __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto gload = [&](int kt) {
+    auto gload = [&](int kt, u32x4 (&ra)[Cfg::A_PER_THREAD], u32x4 (&rb)[Cfg::B_PER_THREAD]) {
         const int k0 = kt * Cfg::BK + c16 * Cfg::VEC;
         const bool kin = k0 < K;
 #pragma unroll
@@ -67,42 +88,51 @@ __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)
         for (int i = 0; i < Cfg::B_PER_THREAD; ++i)
             rb[i] = (b_row[i] != nullptr && kin) ? ld16(b_row[i] + kt * Cfg::BK) : zero;
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, const u32x4 (&ra)[Cfg::A_PER_THREAD], const u32x4 (&rb)[Cfg::B_PER_THREAD]) {
         char* As = lds + buf * Cfg::STAGE_BYTES;
         char* Bs = As + Cfg::A_BYTES;
 #pragma unroll
-        for (int i = 0; i < Cfg::A_PER_THREAD; ++i) st16(As + (tid / 8 + 32 * i) * kPitch + c16 * 16, ra[i]);
+        for (int i = 0; i < Cfg::A_PER_THREAD; ++i) st16(As + tile_off(tid / 8 + 32 * i, c16), ra[i]);
 #pragma unroll
-        for (int i = 0; i < Cfg::B_PER_THREAD; ++i) st16(Bs + (tid / 8 + 32 * i) * kPitch + c16 * 16, rb[i]);
+        for (int i = 0; i < Cfg::B_PER_THREAD; ++i) st16(Bs + tile_off(tid / 8 + 32 * i, c16), rb[i]);
     };
     auto compute = [&](int buf) {
         const char* As = lds + buf * Cfg::STAGE_BYTES;
         const char* Bs = As + Cfg::A_BYTES;
 #pragma unroll
         for (int ks = 0; ks < Cfg::BK / 32; ++ks) {
-            const int kb = (ks * 32 + 8 * (lane >> 4)) * (int)sizeof(T);
+            const int kc = (ks * 32 + 8 * (lane >> 4)) * (int)sizeof(T) / 16;   // 16-byte chunk
             Frag<T> af[Cfg::FM], bfg[Cfg::FN];
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
-                af[i] = ld_frag<T>(As + ((wm * Cfg::FM + i) * 16 + (lane & 15)) * kPitch + kb);
+                af[i] = ld_tile_frag<T>(As, (wm * Cfg::FM + i) * 16 + (lane & 15), kc);
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j)
-                bfg[j] = ld_frag<T>(Bs + ((wn * Cfg::FN + j) * 16 + (lane & 15)) * kPitch + kb);
+                bfg[j] = ld_tile_frag<T>(Bs, (wn * Cfg::FN + j) * 16 + (lane & 15), kc);
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mma16(af[i], bfg[j], acc[i][j]);
         }
     };
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) gload(kt + 1);
+    // Step kt computes from LDS buffer kt%2, refills the register set that
+    // held step kt with step kt+2, and moves step kt+1 (loaded one step ago)
+    // from the other register set into LDS buffer (kt+1)%2.
+    auto step = [&](int kt, u32x4 (&ra_kt)[Cfg::A_PER_THREAD], u32x4 (&rb_kt)[Cfg::B_PER_THREAD],
+                    const u32x4 (&ra_n)[Cfg::A_PER_THREAD], const u32x4 (&rb_n)[Cfg::B_PER_THREAD]) {
+        if (kt + 2 < nk) gload(kt + 2, ra_kt, rb_kt);
         compute(kt & 1);
-        if (kt + 1 < nk) sstore((kt + 1) & 1);
+        if (kt + 1 < nk) sstore((kt + 1) & 1, ra_n, rb_n);
         __syncthreads();
+    };
+
+    gload(0, ra0, rb0);
+    if (nk > 1) gload(1, ra1, rb1);
+    sstore(0, ra0, rb0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, ra0, rb0, ra1, rb1);
+        if (kt + 1 < nk) step(kt + 1, ra1, rb1, ra0, rb0);
     }
 }
 
@@ -163,7 +193,7 @@ struct ProjArgs {
 };
 
 template <typename T, class Cfg>
-__global__ __launch_bounds__(256) void proj_gemm_kernel(ProjArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_gemm_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     const int tid = threadIdx.x;
     const int64_t n_m = (a.M_rows + Cfg::BM - 1) / Cfg::BM;
@@ -279,7 +309,7 @@ struct GroupArgs {
 };
 
 template <typename T, class Cfg>
-__global__ __launch_bounds__(256) void grouped_q_kernel(GroupArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_q_kernel(GroupArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     __shared__ int32_t s_dst[Cfg::BM];
     const int tid = threadIdx.x;
