@@ -70,12 +70,16 @@ constexpr int kAttnNW = GQE_ATTN_NW;
 constexpr int kAttnBKV = GQE_ATTN_BKV;
 constexpr float kLazyRescale = 8.f;   // log2 units the running max may lag by
 
+// Maximum that propagates NaN (IEEE maximum): gfx950 has it as v_maximum3_f32
+// and needs no quieting of the inputs, unlike fmaxf. Scores are never NaN.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max over the four lanes {l16, l16+16, l16+32, l16+48} that hold one query.
 __device__ __forceinline__ float quad_row_max(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const float y = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Key held by row i of 16-row score block kb. The order makes the eight P
@@ -97,6 +101,11 @@ template <int VCH>
 __device__ __forceinline__ int v_chunk_off(int r, int c) {
     return r * VCH * 16 + ((c ^ (r & (VCH - 1))) * 16);
 }
+
+template <int N>
+struct StageC {
+    static constexpr int value = N;
+};
 
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQE_ATTN_WPE, GQE_ATTN_WPE)))
@@ -221,11 +230,17 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) o[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // Reference subtracted from the scores of each query (log2 units);
-    // -inf until the first tile sets it.
-    float mref[QB];
+    // Reference m subtracted from the scores of each query (log2 units),
+    // kept as the C operand that starts every score block (-m, or 0 until the
+    // first tile sets it) and as the rebase threshold (-inf until set, then
+    // kLazyRescale): both change only when the reference moves.
+    f32x4 minit[QB];
+    float thr[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mref[qb] = -INFINITY;
+    for (int qb = 0; qb < QB; ++qb) {
+        minit[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        thr[qb] = -INFINITY;
+    }
 
     // Keys up to the last token of the tile.
     const int t_hi = (int)min<int64_t>(T_ - 1, ((int64_t)qt * BQ + BQ - 1) / Rg);
@@ -286,23 +301,18 @@ void attn_fwd_kernel(AttnArgs a) {
         }
     };
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int j = 0; j < n_kv; ++j) {
+    // One key tile; the LDS stage is a compile-time constant so every LDS
+    // address is a per-lane base plus an immediate offset.
+    auto tile = [&](int j, auto stage) {
+        constexpr int ST = decltype(stage)::value;
         if (j + 1 < n_kv) gload(j + 1);
         const int s0 = j * BKV;
         if (s0 <= t_last) {                    // else every key is above every query of this wave
-            const char* Ks = lds + (j & 1) * STAGE;
+            const char* Ks = lds + ST * STAGE;
             const char* Vs = Ks + K_BYTES;
             // S^T = K Q^T - m, accumulated from the current reference.
             // The first MFMA of every block takes -m as its C operand.
-            f32x4 s[KB][QB], init[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float m0 = (mref[qb] == -INFINITY) ? 0.f : -mref[qb];
-                init[qb] = f32x4{m0, m0, m0, m0};
-            }
+            f32x4 s[KB][QB];
 #pragma unroll
             for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
@@ -316,7 +326,7 @@ void attn_fwd_kernel(AttnArgs a) {
                         kf.hi = *reinterpret_cast<const f32x4*>(Ks + k_chunk_off<KCH>(kr, kc0 + 1));
                     }
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16(kf, qf[qb][dk], dk == 0 ? init[qb] : s[kb][qb]);
+                    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16(kf, qf[qb][dk], dk == 0 ? minit[qb] : s[kb][qb]);
                 }
             if (s0 + BKV - 1 > t_first) {      // a key may lie above a query: causal mask
 #pragma unroll
@@ -335,15 +345,16 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][qb][v]);
+                    for (int v = 0; v < 4; ++v) mx = vmax(mx, s[kb][qb][v]);
                 mx = quad_row_max(mx);
                 // Move the reference only when needed: first tile, or scores
                 // more than kLazyRescale above it.
-                const bool need = (mref[qb] == -INFINITY && mx > -INFINITY) || mx > kLazyRescale;
+                const bool need = mx > thr[qb];
                 if (__builtin_amdgcn_ballot_w64(need) != 0) {
                     const float delta = need ? mx : 0.f;
                     const float corr = __builtin_amdgcn_exp2f(-delta);
-                    mref[qb] = need ? ((mref[qb] == -INFINITY) ? mx : mref[qb] + mx) : mref[qb];
+                    minit[qb] -= delta;
+                    thr[qb] = need ? kLazyRescale : thr[qb];
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) s[kb][qb] -= delta;
 #pragma unroll
@@ -390,8 +401,16 @@ void attn_fwd_kernel(AttnArgs a) {
                 }
             }
         }
-        if (j + 1 < n_kv) sstore((j + 1) & 1);
+        if (j + 1 < n_kv) sstore(ST ^ 1);
         __syncthreads();
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int j = 0; j < n_kv; j += 2) {
+        tile(j, StageC<0>{});
+        if (j + 1 < n_kv) tile(j + 1, StageC<1>{});
     }
 
     // Normalise and store. The denominator sits in row 0 of lsum (lanes of
