@@ -102,6 +102,37 @@ __device__ __forceinline__ int v_chunk_off(int r, int c) {
     return r * VCH * 16 + ((c ^ (r & (VCH - 1))) * 16);
 }
 
+// Placement of the units of one level on the XCDs. Workgroup i runs on XCD
+// i % 8, so slot p of a level whose first workgroup index is c0 runs on XCD
+// (c0 + p) % 8. Regular stream r (a KV group of one sequence, one unit per
+// level) has home XCD r % 8: slot p on XCD x that is the k-th slot of the
+// level on x takes stream x + 8k when it exists. The other slots take, in
+// order, the level's extra units (index nrb + i) and then the regular streams
+// that found no home slot. A bijection of [0, c) for any c >= nrb.
+__device__ __forceinline__ int64_t level_slot_unit(int64_t p, int64_t c, int s0, int64_t nrb) {
+    auto visits = [&](int x, int64_t upto) -> int64_t {   // slots before upto on XCD x
+        const int d = (x - s0) & 7;
+        return upto > d ? (upto - d - 1) / 8 + 1 : 0;
+    };
+    auto homes = [&](int x) -> int64_t { return nrb > x ? (nrb - 1 - x) / 8 + 1 : 0; };
+    const int x = (int)((s0 + p) & 7);
+    const int64_t k = visits(x, p);
+    if (k < homes(x)) return x + 8 * k;
+    int64_t rank = p;                                     // overflow slots before p
+    for (int y = 0; y < 8; ++y) rank -= min(visits(y, p), homes(y));
+    const int64_t nx = c - nrb;
+    if (rank < nx) return nrb + rank;
+    int64_t left = rank - nx;
+    for (int y = 0; y < 8; ++y) {
+        const int64_t lo = visits(y, c), hi = homes(y);
+        if (hi > lo) {
+            if (left < hi - lo) return y + 8 * (lo + left);
+            left -= hi - lo;
+        }
+    }
+    return 0;   // not reached for p < c
+}
+
 template <int N>
 struct StageC {
     static constexpr int value = N;
@@ -141,7 +172,9 @@ void attn_fwd_kernel(AttnArgs a) {
     // token, n_x tiles). Workgroups are ordered by level, longest rows first:
     // level l holds tile n_o-1-l of every regular group and the extra group's
     // tiles that end at about the same token, [n_x - e(l+1), n_x - e(l)) with
-    // e(l) = l*n_x/n_o; count(l) workgroups precede level l.
+    // e(l) = l*n_x/n_o; count(l) workgroups precede level l. Inside a level
+    // the units are placed by level_slot_unit so that each regular stream
+    // stays on one XCD (and one L2) from level to level.
     const bool xcls = a.Q1 != nullptr;
     const int n_reg = xcls ? a.G - 1 : a.G;                // regular groups
     const int64_t nrb = (int64_t)a.Bt * n_reg;              // regular workgroups per level
@@ -153,7 +186,8 @@ void attn_fwd_kernel(AttnArgs a) {
     lv = min(max(lv, 0), a.n_o - 1);
     while (lv > 0 && count(lv) > L) --lv;
     while (lv + 1 < a.n_o && count(lv + 1) <= L) ++lv;
-    const int64_t pos = L - count(lv);
+    const int64_t c0 = count(lv);
+    const int64_t pos = level_slot_unit(L - c0, count(lv + 1) - c0, (int)(c0 & 7), nrb);
     int g, b, qt, Rg;
     if (pos < nrb) {
         const int gi = (int)(pos / a.Bt);
