@@ -28,6 +28,18 @@ CASES = {
     "all_experts": Shape(B=2, T=150, D=128, G=2, M=3, k=3, d=64),
     "multi_tile": Shape(B=2, T=1000, D=256, G=8, M=2, k=1, d=64),
     "wide_pool": Shape(B=1, T=260, D=128, G=4, M=16, k=4, d=32, router_bias=True),
+    # 9 regular KV streams and one or two shared-head tiles per level: some
+    # levels have more streams homed on an XCD than slots landing on it.
+    "many_groups": Shape(B=1, T=300, D=128, G=10, M=4, k=4, d=32),
+}
+
+# Dense GQA layers (Hq = G*M query heads over G KV groups). 3 sequences x 3
+# groups = 9 KV streams: the attention grid's placement then has to hand some
+# streams to slots away from their home XCD.
+GQA_CASES = {
+    "gqa_9_streams": Shape(B=3, T=600, D=128, G=3, M=2, k=1, d=32),
+    "gqa_ragged_f32": Shape(B=2, T=333, D=64, G=1, M=4, k=1, d=64, dtype="f32"),
+    "gqa_wide": Shape(B=1, T=515, D=256, G=5, M=3, k=1, d=64),
 }
 
 
@@ -96,6 +108,22 @@ def test_small_layer_full_parity(name):
     assert err <= bound, (name, "slots", err, bound)
     err, bound = H.out_error(H.np32(out2), ref["out"])
     assert err <= bound, (name, "routed out", err, bound)
+
+
+@pytest.mark.parametrize("name", sorted(GQA_CASES))
+def test_small_gqa_full_parity(name):
+    s = GQA_CASES[name]
+    inp = make_inputs(s, seed=11 + len(name))
+    f = H.f64_inputs(inp)
+    dv = H.to_device(inp)
+    print(f"[gqa case {name}] {s}", flush=True)
+    ga = go.gqa_forward(dict(x=f["x"], Wq=f["Wq"], Wk=f["Wk"], Wv=f["Wv"], Wo=f["Wo_gqa"]),
+                        s.G, s.Hq, s.d, s.B, s.T)
+    og = torch.empty(s.N, s.D, dtype=s.torch_dtype(), device="cuda")
+    H.run_gqa(s, dv, og)
+    torch.cuda.synchronize()
+    err, bound = H.out_error(H.np32(og), ga["out"])
+    assert err <= bound, (name, err, bound)
 
 
 @pytest.mark.parametrize("cid", [1, 2])
