@@ -47,20 +47,24 @@ struct TileCfg {
     static constexpr int A_BYTES = BM * kPitch;
     static constexpr int B_BYTES = BN * kPitch;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int SP = BN + 4;                   // fp32 pitch of the epilogue stage
-    static constexpr int LDS_BYTES =
-        (2 * STAGE_BYTES > BM * SP * 4) ? 2 * STAGE_BYTES : BM * SP * 4;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
     static_assert(WM * WN == 4, "256 threads = 4 waves");
     static_assert(BM * 8 % 256 == 0 && BN * 8 % 256 == 0, "tile rows must split over 256 threads");
 };
 
 // K loop. a_row[i] / b_row[i] point at the tile rows this thread loads
-// (row tid/8 + 32*i), already offset by its 16-byte column chunk; nullptr
-// rows read as zeros, as do columns at or beyond K. Global loads run two K
-// steps ahead of the MFMAs (two register sets), LDS holds two steps. Leaves
-// the C block of this wave in acc and the LDS free (all waves past the final
-// barrier).
-template <typename T, class Cfg>
+// (row tid/8 + 32*i), already offset by its 16-byte column chunk. Every
+// pointer must be readable for the whole K range: rows outside the problem
+// point at some valid row instead (their results are never stored), so the
+// loads need no branches. Chunks at or beyond K (only in a partial last step)
+// read A as zero and B from the row's first chunk, so they add nothing.
+// Global loads run two K steps ahead of the MFMAs (two register sets), LDS
+// holds two steps. Leaves the C block of this wave in acc and the LDS free
+// (all waves past the final barrier). In 16x16 block (i, j) of the wave a
+// lane holds 4 consecutive entries along one line of C: without SWAP, rows
+// 4*(lane/16) .. +3 of column lane%16 (acc = A-block x B-block^T); with SWAP
+// the transposed block, i.e. columns 4*(lane/16) .. +3 of row lane%16.
+template <typename T, class Cfg, bool SWAP>
 __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)[Cfg::A_PER_THREAD],
                                               const T* const (&b_row)[Cfg::B_PER_THREAD], int K,
                                               f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
@@ -79,14 +83,22 @@ __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)
         for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto gload = [&](int kt, u32x4 (&ra)[Cfg::A_PER_THREAD], u32x4 (&rb)[Cfg::B_PER_THREAD]) {
-        const int k0 = kt * Cfg::BK + c16 * Cfg::VEC;
-        const bool kin = k0 < K;
+        if ((kt + 1) * Cfg::BK <= K) {        // whole step inside K
 #pragma unroll
-        for (int i = 0; i < Cfg::A_PER_THREAD; ++i)
-            ra[i] = (a_row[i] != nullptr && kin) ? ld16(a_row[i] + kt * Cfg::BK) : zero;
+            for (int i = 0; i < Cfg::A_PER_THREAD; ++i) ra[i] = ld16(a_row[i] + kt * Cfg::BK);
 #pragma unroll
-        for (int i = 0; i < Cfg::B_PER_THREAD; ++i)
-            rb[i] = (b_row[i] != nullptr && kin) ? ld16(b_row[i] + kt * Cfg::BK) : zero;
+            for (int i = 0; i < Cfg::B_PER_THREAD; ++i) rb[i] = ld16(b_row[i] + kt * Cfg::BK);
+        } else {
+            const bool kin = kt * Cfg::BK + c16 * Cfg::VEC < K;
+            const int ko = kin ? kt * Cfg::BK : 0;
+#pragma unroll
+            for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
+                const u32x4 v = ld16(a_row[i] + ko);
+                ra[i] = kin ? v : zero;
+            }
+#pragma unroll
+            for (int i = 0; i < Cfg::B_PER_THREAD; ++i) rb[i] = ld16(b_row[i] + ko);
+        }
     };
     auto sstore = [&](int buf, const u32x4 (&ra)[Cfg::A_PER_THREAD], const u32x4 (&rb)[Cfg::B_PER_THREAD]) {
         char* As = lds + buf * Cfg::STAGE_BYTES;
@@ -112,7 +124,8 @@ __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mma16(af[i], bfg[j], acc[i][j]);
+                for (int j = 0; j < Cfg::FN; ++j)
+                    acc[i][j] = SWAP ? mma16(bfg[j], af[i], acc[i][j]) : mma16(af[i], bfg[j], acc[i][j]);
         }
     };
     // Step kt computes from LDS buffer kt%2, refills the register set that
@@ -136,30 +149,32 @@ __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)
     }
 }
 
-// Writes this wave's C block to the fp32 LDS stage [BM][SP] and waits for
-// all waves. Call after gemm_mainloop.
-template <class Cfg>
-__device__ __forceinline__ void stage_acc(float* stage, const f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = (wm * Cfg::FM + i) * 16 + 4 * (lane >> 4) + v;
-                const int col = (wn * Cfg::FN + j) * 16 + (lane & 15);
-                stage[row * Cfg::SP + col] = acc[i][j][v];
-            }
-    __syncthreads();
-}
-
 // ---------------------------------------------------------------------------
 // Multi-block projection: out_s = A W_s^T for up to 4 weight blocks W_s laid
 // side by side as one virtual weight matrix (block s starts at virtual column
-// col_begin, a multiple of 8).
+// col_begin, a multiple of 8). A block whose output is transposed
+// (OUT_HEADS_T) never shares a column tile with a row-major block: the host
+// starts a block at a multiple of kProjClassAlign whenever the class changes.
+// Each tile then writes straight from the accumulators, oriented so that a
+// lane's four consecutive values run along the output's contiguous axis.
 // ---------------------------------------------------------------------------
+constexpr int kProjClassAlign = 128;
+
+// Four consecutive outputs from an accumulator, scaled (8 bytes bf16, 16
+// fp32), as a non-temporal store: projection outputs are read by a later
+// kernel, and keeping them out of L2 leaves it to the weight and activation
+// tiles the GEMM re-reads (measured faster for the step as a whole).
+template <typename T>
+__device__ __forceinline__ void store4(T* o, const f32x4& v, float scale) {
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (bf16)(v[q] * scale);
+        __builtin_nontemporal_store(__builtin_bit_cast(uint64_t, w), reinterpret_cast<uint64_t*>(o));
+    } else {
+        __builtin_nontemporal_store(v * scale, reinterpret_cast<f32x4*>(o));
+    }
+}
 enum OutMode : int32_t {
     OUT_ROWS = 0,      // out[row * ld_out + col], type T
     OUT_ROWS_F32 = 1,  // out[row * ld_out + col] + bias[col], fp32
@@ -193,11 +208,10 @@ struct ProjArgs {
 };
 
 template <typename T, class Cfg>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_gemm_kernel(ProjArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+__device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds, int64_t hw) {
     const int tid = threadIdx.x;
     const int64_t n_m = (a.M_rows + Cfg::BM - 1) / Cfg::BM;
-    const int64_t L = xcd_logical_id(blockIdx.x, n_m * a.n_tiles_n);
+    const int64_t L = xcd_logical_id(hw, n_m * a.n_tiles_n);
     const int64_t m0 = (L / a.n_tiles_n) * Cfg::BM;
     const int n0 = (int)(L % a.n_tiles_n) * Cfg::BN;
 
@@ -206,85 +220,179 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
         const int64_t r = m0 + tid / 8 + 32 * i;
-        a_row[i] = r < a.M_rows ? (const T*)a.A + r * a.lda + (tid & 7) * Cfg::VEC : nullptr;
+        a_row[i] = (const T*)a.A + (r < a.M_rows ? r : m0) * a.lda + (tid & 7) * Cfg::VEC;
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_THREAD; ++i) {
         const int vc = n0 + tid / 8 + 32 * i;
-        b_row[i] = nullptr;
+        b_row[i] = (const T*)a.seg[0].W + (tid & 7) * Cfg::VEC;   // columns past every block
         for (int s = 0; s < a.n_segs; ++s) {
             const int c = vc - a.seg[s].col_begin;
             if (c >= 0 && c < a.seg[s].n_cols)
                 b_row[i] = (const T*)a.seg[s].W + (int64_t)c * a.K + (tid & 7) * Cfg::VEC;
         }
     }
-    f32x4 acc[Cfg::FM][Cfg::FN];
-    gemm_mainloop<T, Cfg>(lds, a_row, b_row, a.K, acc);
-    float* stage = reinterpret_cast<float*>(lds);
-    stage_acc<Cfg>(stage, acc);
+    static_assert(kProjClassAlign % Cfg::BN == 0, "a column tile holds one output class");
 
-    // Row-vector modes: 8 consecutive columns of one row per item.
-    constexpr int CCH = Cfg::BN / 8;
-    for (int it = tid; it < Cfg::BM * CCH; it += 256) {
-        const int r = it / CCH, cc = (it % CCH) * 8;
-        const int64_t row = m0 + r;
-        const int vc = n0 + cc;
-        if (row >= a.M_rows) continue;
+    // Sequence b and token t of tile row r (token row n = b*T + t), from one
+    // division per tile.
+    const int64_t b0 = m0 / a.T, t0 = m0 - b0 * a.T;
+    auto split = [&](int r, int64_t& b, int64_t& t) {
+        t = t0 + r;
+        b = b0;
+        while (t >= a.T) {
+            t -= a.T;
+            ++b;
+        }
+    };
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    const int log2d = 31 - __builtin_clz(a.d);            // head widths are powers of two
+    bool trans = false;
+    for (int s = 0; s < a.n_segs; ++s)
+        if (a.seg[s].col_begin <= n0 && n0 < a.seg[s].col_begin + a.seg[s].n_cols) trans = a.seg[s].mode == OUT_HEADS_T;
+    f32x4 acc[Cfg::FM][Cfg::FN];
+    // Fast path: every row of the tile is a token of one sequence, one block
+    // covers all of the tile's columns, and vector stores are aligned; each
+    // lane then stores its 16 quads at fixed offsets from one base pointer.
+    int full_seg = -1;
+    for (int s = 0; s < a.n_segs; ++s)
+        if (a.seg[s].col_begin <= n0 && n0 + Cfg::BN <= a.seg[s].col_begin + a.seg[s].n_cols) full_seg = s;
+    const bool fast = full_seg >= 0 && m0 + Cfg::BM <= a.M_rows && t0 + Cfg::BM <= a.T && (t0 & 3) == 0 &&
+                      (reinterpret_cast<uintptr_t>(a.seg[full_seg].out) & 15) == 0 &&
+                      (a.seg[full_seg].mode != OUT_ROWS || (a.seg[full_seg].ld_out & 3) == 0) &&
+                      a.seg[full_seg].mode != OUT_ROWS_F32;
+
+    if (trans) {
+        // Transposed heads: a lane holds tokens r .. r+3 of column c.
+        gemm_mainloop<T, Cfg, false>(lds, a_row, b_row, a.K, acc);
+        const int64_t ldo = (int64_t)a.Bt * a.Tpad;
+        if (fast) {
+            const ProjSeg& sg = a.seg[full_seg];
+            const int c0 = n0 - sg.col_begin + wn * Cfg::FN * 16 + (lane & 15);
+            T* p = (T*)sg.out + (int64_t)c0 * ldo + b0 * a.Tpad + t0 + wm * Cfg::FM * 16 + 4 * (lane >> 4);
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i) store4<T>(p + (int64_t)j * 16 * ldo + i * 16, acc[i][j], sg.scale);
+            return;
+        }
         for (int s = 0; s < a.n_segs; ++s) {
             const ProjSeg& sg = a.seg[s];
-            const int c = vc - sg.col_begin;
-            if (c < 0 || c >= sg.n_cols || sg.mode == OUT_HEADS_T) continue;
-            float v[8];
+            if (sg.col_begin >= n0 + Cfg::BN || sg.col_begin + sg.n_cols <= n0) continue;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = stage[r * Cfg::SP + cc + q] * sg.scale;
-            const int nv = min(8, sg.n_cols - c);
-            if (sg.mode == OUT_ROWS_F32) {
-                float* o = (float*)sg.out + row * sg.ld_out + c;
-                for (int q = 0; q < nv; ++q) o[q] = v[q] + (sg.bias ? sg.bias[c + q] : 0.f);
-            } else {
-                T* o;
-                if (sg.mode == OUT_ROWS) {
-                    o = (T*)sg.out + row * sg.ld_out + c;
-                } else {  // OUT_HEADS
-                    const int64_t b = row / a.T, t = row % a.T;
-                    o = (T*)sg.out + (((int64_t)(c / a.d) * a.Bt + b) * a.Tpad + t) * a.d + (c % a.d);
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j) {
+                    const int c = n0 + (wn * Cfg::FN + j) * 16 + (lane & 15) - sg.col_begin;
+                    const int r = (wm * Cfg::FM + i) * 16 + 4 * (lane >> 4);
+                    if (c < 0 || c >= sg.n_cols || m0 + r >= a.M_rows) continue;
+                    int64_t b, t;
+                    split(r, b, t);
+                    T* o = (T*)sg.out + (int64_t)c * ldo + b * a.Tpad + t;
+                    if (t + 3 < a.T && m0 + r + 3 < a.M_rows && (t & 3) == 0) {
+                        if constexpr (sizeof(T) == 2) {
+                            bf16x4 w;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) w[v] = (bf16)(acc[i][j][v] * sg.scale);
+                            *reinterpret_cast<bf16x4*>(o) = w;
+                        } else {
+                            *reinterpret_cast<f32x4*>(o) = acc[i][j] * sg.scale;
+                        }
+                    } else {
+                        for (int v = 0; v < 4 && m0 + r + v < a.M_rows; ++v) {
+                            int64_t bv, tv;
+                            split(r + v, bv, tv);
+                            ((T*)sg.out)[(int64_t)c * ldo + bv * a.Tpad + tv] = from_f32<T>(acc[i][j][v] * sg.scale);
+                        }
+                    }
                 }
-                if (nv == 8) {
-                    store8<T>(o, v);
-                } else {
-                    for (int q = 0; q < nv; ++q) o[q] = from_f32<T>(v[q]);
-                }
+        }
+        return;
+    }
+
+    // Row-major outputs: a lane holds columns c .. c+3 of row r.
+    gemm_mainloop<T, Cfg, true>(lds, a_row, b_row, a.K, acc);
+    if (fast) {
+        const ProjSeg& sg = a.seg[full_seg];
+        const int c0 = n0 - sg.col_begin + wn * Cfg::FN * 16 + 4 * (lane >> 4);
+        const int r0 = wm * Cfg::FM * 16 + (lane & 15);
+        if (sg.mode == OUT_ROWS) {
+            T* p = (T*)sg.out + (m0 + r0) * sg.ld_out + c0;
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j) store4<T>(p + (int64_t)i * 16 * sg.ld_out + j * 16, acc[i][j], sg.scale);
+        } else {   // OUT_HEADS: token rows of one sequence, d-wide head rows
+            const int64_t hstride = (int64_t)a.Bt * a.Tpad * a.d;
+            T* p = (T*)sg.out + (b0 * a.Tpad + t0 + r0) * a.d;
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const int c = c0 + 16 * j;
+                T* pj = p + (int64_t)(c >> log2d) * hstride + (c & (a.d - 1));
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i) store4<T>(pj + i * 16 * a.d, acc[i][j], sg.scale);
             }
         }
+        return;
     }
-    // Column-vector mode: 8 consecutive rows (tokens) of one column per item.
-    constexpr int RCH = Cfg::BM / 8;
     for (int s = 0; s < a.n_segs; ++s) {
         const ProjSeg& sg = a.seg[s];
-        if (sg.mode != OUT_HEADS_T) continue;
-        for (int it = tid; it < Cfg::BN * RCH; it += 256) {
-            const int cl = it / RCH, rr = (it % RCH) * 8;
-            const int c = n0 + cl - sg.col_begin;
-            if (c < 0 || c >= sg.n_cols) continue;
-            const int64_t row = m0 + rr;
-            if (row >= a.M_rows) continue;
-            const int64_t b = row / a.T, t = row % a.T;
-            T* o = (T*)sg.out + ((int64_t)(c / a.d) * a.d + (c % a.d)) * (a.Bt * a.Tpad) + b * a.Tpad + t;
-            float v[8];
+        if (sg.col_begin >= n0 + Cfg::BN || sg.col_begin + sg.n_cols <= n0) continue;
+        const bool vec_ok = (reinterpret_cast<uintptr_t>(sg.out) & 15) == 0 && (sg.mode == OUT_HEADS || (sg.ld_out & 3) == 0);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = stage[(rr + q) * Cfg::SP + cl] * sg.scale;
-            if (row + 8 <= a.M_rows && t + 8 <= a.T && (t % 8) == 0) {
-                store8<T>(o, v);
-            } else {
-                for (int q = 0; q < 8 && row + q < a.M_rows; ++q) {
-                    const int64_t rq = row + q, bq = rq / a.T, tq = rq % a.T;
-                    T* oq = (T*)sg.out + ((int64_t)(c / a.d) * a.d + (c % a.d)) * (a.Bt * a.Tpad) +
-                            bq * a.Tpad + tq;
-                    *oq = from_f32<T>(v[q]);
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const int r = (wm * Cfg::FM + i) * 16 + (lane & 15);
+            const int64_t row = m0 + r;
+            if (row >= a.M_rows) continue;
+            int64_t b = 0, t = 0;
+            if (sg.mode == OUT_HEADS) split(r, b, t);
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const int c = n0 + (wn * Cfg::FN + j) * 16 + 4 * (lane >> 4) - sg.col_begin;
+                if (c < 0 || c >= sg.n_cols) continue;
+                const f32x4 v = acc[i][j] * sg.scale;
+                const bool full = c + 4 <= sg.n_cols;
+                if (sg.mode == OUT_ROWS_F32) {
+                    float* o = (float*)sg.out + row * sg.ld_out + c;
+                    float w4[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w4[q] = v[q] + ((sg.bias && c + q < sg.n_cols) ? sg.bias[c + q] : 0.f);
+                    if (full && vec_ok) {
+                        *reinterpret_cast<f32x4*>(o) = f32x4{w4[0], w4[1], w4[2], w4[3]};
+                    } else {
+                        for (int q = 0; q < 4 && c + q < sg.n_cols; ++q) o[q] = w4[q];
+                    }
+                    continue;
+                }
+                T* o = sg.mode == OUT_ROWS
+                           ? (T*)sg.out + row * sg.ld_out + c
+                           : (T*)sg.out + ((((int64_t)(c >> log2d)) * a.Bt + b) * a.Tpad + t) * a.d + (c & (a.d - 1));
+                if (full && vec_ok) {
+                    if constexpr (sizeof(T) == 2) {
+                        bf16x4 w;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) w[q] = (bf16)v[q];
+                        *reinterpret_cast<bf16x4*>(o) = w;
+                    } else {
+                        *reinterpret_cast<f32x4*>(o) = v;
+                    }
+                } else {
+                    for (int q = 0; q < 4 && c + q < sg.n_cols; ++q) o[q] = from_f32<T>(v[q]);
                 }
             }
         }
     }
+}
+
+// Persistent grid: workgroup b handles tiles b, b + gridDim.x, ... (grid a
+// multiple of 8, so every tile index keeps its XCD), which lets one tile's
+// stores drain while the next tile's K loop runs.
+template <typename T, class Cfg>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_gemm_kernel(ProjArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+    const int64_t n = ((a.M_rows + Cfg::BM - 1) / Cfg::BM) * a.n_tiles_n;
+    for (int64_t hw = blockIdx.x; hw < n; hw += gridDim.x) proj_tile<T, Cfg>(a, lds, hw);
 }
 
 // ---------------------------------------------------------------------------
@@ -312,7 +420,8 @@ template <typename T, class Cfg>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_q_kernel(GroupArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     __shared__ int32_t s_dst[Cfg::BM];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int64_t L = xcd_logical_id(blockIdx.x, (int64_t)a.nC * a.E);
     const int c = (int)(L / a.E), e = (int)(L % a.E);
     const int rb = a.cbase[(int64_t)c * a.E + e];
@@ -322,31 +431,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_THREAD; ++i) {
         const int j = tid / 8 + 32 * i;
-        b_row[i] = j < a.d ? (const T*)a.Wq + ((int64_t)e * a.d + j) * a.K + (tid & 7) * Cfg::VEC : nullptr;
+        b_row[i] = (const T*)a.Wq + ((int64_t)e * a.d + (j < a.d ? j : 0)) * a.K + (tid & 7) * Cfg::VEC;
     }
     for (int r0 = rb; r0 < re; r0 += Cfg::BM) {
         const T* a_row[Cfg::A_PER_THREAD];
 #pragma unroll
         for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
             const int r = r0 + tid / 8 + 32 * i;
-            a_row[i] = r < re ? (const T*)a.X + (int64_t)a.perm[r] * a.ldx + (tid & 7) * Cfg::VEC : nullptr;
+            a_row[i] = (const T*)a.X + (int64_t)a.perm[r < re ? r : rb] * a.ldx + (tid & 7) * Cfg::VEC;
         }
         for (int r = tid; r < Cfg::BM; r += 256) s_dst[r] = (r0 + r < re) ? a.dst[r0 + r] : -1;
+        // Transposed blocks: a lane holds output columns c .. c+3 of tile row r.
         f32x4 acc[Cfg::FM][Cfg::FN];
-        gemm_mainloop<T, Cfg>(lds, a_row, b_row, a.K, acc);
-        float* stage = reinterpret_cast<float*>(lds);
-        stage_acc<Cfg>(stage, acc);
-        constexpr int CCH = Cfg::BN / 8;
-        for (int it = tid; it < Cfg::BM * CCH; it += 256) {
-            const int r = it / CCH, cc = (it % CCH) * 8;
-            const int drow = s_dst[r];
-            if (drow < 0 || cc >= a.d) continue;
-            float v[8];
+        gemm_mainloop<T, Cfg, true>(lds, a_row, b_row, a.K, acc);   // ends with a barrier: s_dst is visible
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = stage[r * Cfg::SP + cc + q] * a.scale;
-            store8<T>((T*)a.Qr + (int64_t)drow * a.d + cc, v);
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const int drow = s_dst[(wm * Cfg::FM + i) * 16 + (lane & 15)];
+            if (drow < 0) continue;
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const int col = (wn * Cfg::FN + j) * 16 + 4 * (lane >> 4);
+                if (col >= a.d) continue;
+                const f32x4 v = acc[i][j] * a.scale;
+                T* o = (T*)a.Qr + (int64_t)drow * a.d + col;
+                if constexpr (sizeof(T) == 2) {
+                    bf16x4 w;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[q] = (bf16)v[q];
+                    *reinterpret_cast<bf16x4*>(o) = w;
+                } else {
+                    *reinterpret_cast<f32x4*>(o) = v;
+                }
+            }
         }
-        __syncthreads();  // the stage and s_dst are reused by the next row tile
+        __syncthreads();  // s_dst is reused by the next row tile
     }
 }
 

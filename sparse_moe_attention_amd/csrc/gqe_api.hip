@@ -15,6 +15,7 @@
 //   proj      C Wo^T -> out                                          [MFMA]
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -103,11 +104,27 @@ inline char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
 template <typename T, class Cfg>
 void launch_proj(ProjArgs& a, int total_cols, hipStream_t st) {
     a.n_tiles_n = (total_cols + Cfg::BN - 1) / Cfg::BN;
     const int64_t n_m = (a.M_rows + Cfg::BM - 1) / Cfg::BM;
-    hipLaunchKernelGGL((proj_gemm_kernel<T, Cfg>), dim3((unsigned)(n_m * a.n_tiles_n)), dim3(256), 0, st, a);
+    // Two resident workgroups per CU (LDS and register budget), rounded to
+    // whole XCD rounds.
+    const int64_t tiles = n_m * a.n_tiles_n;
+    const int64_t grid = std::min<int64_t>(tiles, 2 * (int64_t)align_up((size_t)device_cus(), 8));
+    hipLaunchKernelGGL((proj_gemm_kernel<T, Cfg>), dim3((unsigned)grid), dim3(256), 0, st, a);
 }
 
 struct SegList {
@@ -115,6 +132,9 @@ struct SegList {
     int cols = 0;
     void add(const void* W, int n_cols, void* out, int mode, int64_t ld_out, const float* bias,
              float scale = 1.f) {
+        // A transposed block never shares a column tile with a row-major one.
+        if (a.n_segs > 0 && (a.seg[a.n_segs - 1].mode == OUT_HEADS_T) != (mode == OUT_HEADS_T))
+            cols = (int)align_up((size_t)cols, kProjClassAlign);
         ProjSeg& s = a.seg[a.n_segs++];
         s.W = W;
         s.out = out;
@@ -210,8 +230,8 @@ gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* 
     if (project_kv) {
         SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
         sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
-        sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
         sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
+        sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
         run_proj(d, sl, st);
     }
     int32_t* cbase = (int32_t*)at(ws, L.cbase);
@@ -328,9 +348,9 @@ gqe_status gqe_attn_fwd_timed(const gqe_shape* s, const void* x, const void* Wr,
     // One pass over x: K, V^T, Q_sh and the router logits.
     SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
     sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
-    sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
     sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
     sl.add(Wr, d.E, lg, OUT_ROWS_F32, d.E, br);
+    sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
     run_proj(d, sl, st);
     mk.at(1);
     hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)lg, idx, w,
@@ -400,8 +420,8 @@ gqe_status gqa_attn_fwd_timed(int64_t B, int64_t T, int64_t D, int32_t Hq, int32
     mk.at(0);
     SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
     sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
-    sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
     sl.add(Wq, Hq * d.d, at(ws, L.Q), OUT_ROWS, qld, nullptr, q_scale(d));
+    sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
     run_proj(d, sl, st);
     AttnArgs a;
     std::memset(&a, 0, sizeof(a));
