@@ -396,10 +396,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Sparse Q projection as a grouped GEMM. Workgroup (chunk c, expert e)
-// handles rows [cbase[c][e], cbase[c+1][e]) of expert e's segment of the
-// permutation: the tokens of chunk c that picked e, in token order. Each
-// row computes x[perm[i]] Wq_e^T and stores it at row dst[i] of Qr [*, d].
+// Sparse Q projection as a grouped GEMM. Expert e's picks form the segment
+// [cbase[0][e], cbase[nC][e]) of the permutation, in token order; a
+// workgroup takes BM consecutive rows of one segment (tile t of expert e),
+// computes x[perm[i]] Wq_e^T for them and stores row i at row dst[i] of
+// Qr [*, d]. Placement: workgroup hw runs on XCD x = hw % 8 and takes tile
+// t = 8*(j / E) + x of expert j % E, j = hw / 8, so the E experts' tiles with
+// the same index (about the same tokens, since every segment is in token
+// order) run on one XCD and share x rows in its L2, and the non-empty tiles
+// (small t) spread evenly over the XCDs. Tiles past the end of a segment exit.
+// An expert is picked at most once per token, so ceil(N / BM) tiles bound
+// every segment.
 // ---------------------------------------------------------------------------
 struct GroupArgs {
     const void* X;            // [N, K]
@@ -407,12 +414,13 @@ struct GroupArgs {
     void* Qr;                 // [N*G*k, d]
     const int32_t* perm;
     const int32_t* dst;
-    const int32_t* cbase;     // [nC+1][E]
+    const int32_t* cbase;     // [nC+1][E]: row 0 = segment starts, row nC = segment ends
     int64_t ldx;
     int32_t K;
     int32_t d;
     int32_t E;
     int32_t nC;
+    int32_t n_t;              // tiles per expert (bound)
     float scale;              // multiplies the fp32 result before rounding
 };
 
@@ -422,49 +430,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ int32_t s_dst[Cfg::BM];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
-    const int64_t L = xcd_logical_id(blockIdx.x, (int64_t)a.nC * a.E);
-    const int c = (int)(L / a.E), e = (int)(L % a.E);
-    const int rb = a.cbase[(int64_t)c * a.E + e];
-    const int re = a.cbase[(int64_t)(c + 1) * a.E + e];
+    const int64_t j = blockIdx.x / 8;
+    const int t = (int)(8 * (j / a.E) + blockIdx.x % 8), e = (int)(j % a.E);
+    const int sb = a.cbase[e], se = a.cbase[(int64_t)a.nC * a.E + e];
+    const int64_t rb64 = (int64_t)sb + (int64_t)t * Cfg::BM;
+    if (rb64 >= se) return;
+    const int rb = (int)rb64, re = min(se, rb + Cfg::BM);
 
     const T* b_row[Cfg::B_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_THREAD; ++i) {
-        const int j = tid / 8 + 32 * i;
-        b_row[i] = (const T*)a.Wq + ((int64_t)e * a.d + (j < a.d ? j : 0)) * a.K + (tid & 7) * Cfg::VEC;
+        const int jj = tid / 8 + 32 * i;
+        b_row[i] = (const T*)a.Wq + ((int64_t)e * a.d + (jj < a.d ? jj : 0)) * a.K + (tid & 7) * Cfg::VEC;
     }
-    for (int r0 = rb; r0 < re; r0 += Cfg::BM) {
-        const T* a_row[Cfg::A_PER_THREAD];
+    const T* a_row[Cfg::A_PER_THREAD];
 #pragma unroll
-        for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
-            const int r = r0 + tid / 8 + 32 * i;
-            a_row[i] = (const T*)a.X + (int64_t)a.perm[r < re ? r : rb] * a.ldx + (tid & 7) * Cfg::VEC;
-        }
-        for (int r = tid; r < Cfg::BM; r += 256) s_dst[r] = (r0 + r < re) ? a.dst[r0 + r] : -1;
-        // Transposed blocks: a lane holds output columns c .. c+3 of tile row r.
-        f32x4 acc[Cfg::FM][Cfg::FN];
-        gemm_mainloop<T, Cfg, true>(lds, a_row, b_row, a.K, acc);   // ends with a barrier: s_dst is visible
+    for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
+        const int r = rb + tid / 8 + 32 * i;
+        a_row[i] = (const T*)a.X + (int64_t)a.perm[r < re ? r : rb] * a.ldx + (tid & 7) * Cfg::VEC;
+    }
+    for (int r = tid; r < Cfg::BM; r += 256) s_dst[r] = (rb + r < re) ? a.dst[rb + r] : -1;
+    // Swapped operands: a lane holds output columns c .. c+3 of tile row r.
+    f32x4 acc[Cfg::FM][Cfg::FN];
+    gemm_mainloop<T, Cfg, true>(lds, a_row, b_row, a.K, acc);   // its barriers publish s_dst
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) {
-            const int drow = s_dst[(wm * Cfg::FM + i) * 16 + (lane & 15)];
-            if (drow < 0) continue;
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const int drow = s_dst[(wm * Cfg::FM + i) * 16 + (lane & 15)];
+        if (drow < 0) continue;
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j) {
-                const int col = (wn * Cfg::FN + j) * 16 + 4 * (lane >> 4);
-                if (col >= a.d) continue;
-                const f32x4 v = acc[i][j] * a.scale;
-                T* o = (T*)a.Qr + (int64_t)drow * a.d + col;
-                if constexpr (sizeof(T) == 2) {
-                    bf16x4 w;
+        for (int jb = 0; jb < Cfg::FN; ++jb) {
+            const int col = (wn * Cfg::FN + jb) * 16 + 4 * (lane >> 4);
+            if (col >= a.d) continue;
+            const f32x4 v = acc[i][jb] * a.scale;
+            T* o = (T*)a.Qr + (int64_t)drow * a.d + col;
+            if constexpr (sizeof(T) == 2) {
+                bf16x4 w;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) w[q] = (bf16)v[q];
-                    *reinterpret_cast<bf16x4*>(o) = w;
-                } else {
-                    *reinterpret_cast<f32x4*>(o) = v;
-                }
+                for (int q = 0; q < 4; ++q) w[q] = (bf16)v[q];
+                *reinterpret_cast<bf16x4*>(o) = w;
+            } else {
+                *reinterpret_cast<f32x4*>(o) = v;
             }
         }
-        __syncthreads();  // s_dst is reused by the next row tile
     }
 }
 

@@ -177,7 +177,10 @@ void run_grouped_q(const Dims& d, const void* x, const void* Wq, void* Qr, const
     g.X = x; g.Wq = Wq; g.Qr = Qr; g.perm = perm; g.dst = dst; g.cbase = cbase;
     g.ldx = d.D; g.K = (int)d.D; g.d = d.d; g.E = d.E; g.nC = (int)d.nC;
     g.scale = q_scale(d);
-    const dim3 grid((unsigned)(d.nC * d.E));
+    const int bm = d.f32 ? GrpF32::BM : GrpBf16::BM;
+    g.n_t = (int)((d.N + bm - 1) / bm);
+    // 8 * E * ceil(n_t / 8) workgroups: tile t = 8*(j/E) + hw%8 of expert j%E, j = hw/8.
+    const dim3 grid((unsigned)(8 * (int64_t)d.E * ((g.n_t + 7) / 8)));
     if (d.f32) hipLaunchKernelGGL((grouped_q_kernel<float, GrpF32>), grid, dim3(256), 0, st, g);
     else hipLaunchKernelGGL((grouped_q_kernel<bf16, GrpBf16>), grid, dim3(256), 0, st, g);
 }
