@@ -41,8 +41,26 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+    missing = undefined_kernel_stubs(tmp)
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("hipcc dropped the host side of these kernels (a device-only construct in the "
+                           "body failed to compile for the host pass):\n  " + "\n  ".join(missing))
     os.replace(tmp, OUT)
     return OUT
+
+
+def undefined_kernel_stubs(lib: str) -> list[str]:
+    """Kernel launch stubs the library references but does not define.
+
+    hipcc's host pass drops a kernel template instance without a diagnostic
+    when its body does not compile for the host; the library then links but
+    fails to load. An undefined __device_stub__ symbol is that case."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    res = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}: {res.stderr}")
+    return [ln.split()[-1] for ln in res.stdout.splitlines() if "__device_stub__" in ln]
 
 
 if __name__ == "__main__":

@@ -154,10 +154,14 @@ void attn_fwd_kernel(AttnArgs a) {
     constexpr int VCH = BKV * ES / 16;         // 16-byte chunks per V^T row
     constexpr int K_BYTES = BKV * KCH * 16, V_BYTES = D * VCH * 16;
     constexpr int STAGE = K_BYTES + V_BYTES;
-    constexpr int K_PER_T = (BKV * KCH + NT - 1) / NT;
-    constexpr int V_PER_T = (D * VCH + NT - 1) / NT;
+    constexpr int K_PER_T = BKV * KCH / NT;    // 16-byte chunks each thread stages per tile
+    constexpr int V_PER_T = D * VCH / NT;
+    static_assert(BKV * KCH % NT == 0 && D * VCH % NT == 0, "a tile splits evenly over the threads");
     constexpr int VEC = 16 / ES;
-    __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+    // Two LDS stages as separate arrays: the compiler can then tell reads of
+    // one stage from the direct global->LDS loads filling the other.
+    __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
+    __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // The wave index is uniform across the wave; saying so keeps everything
@@ -280,69 +284,68 @@ void attn_fwd_kernel(AttnArgs a) {
     const int t_hi = (int)min<int64_t>(T_ - 1, ((int64_t)qt * BQ + BQ - 1) / Rg);
     const int n_kv = t_hi / BKV + 1;
 
-    u32x4 rk[K_PER_T], rv[V_PER_T];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    constexpr bool K_EXACT = (BKV * KCH) % NT == 0, V_EXACT = (D * VCH) % NT == 0;
-    auto gload = [&](int j) {
-        const int s0 = j * BKV;
-        if (s0 + BKV <= T_ && K_EXACT && V_EXACT) {   // interior tile: no bounds to check
+    // Tiles are staged with gfx950's direct global->LDS loads: one
+    // instruction moves 16 bytes per lane into 64 consecutive 16-byte LDS
+    // slots of the wave, so each lane loads the global chunk that the
+    // swizzled layout puts in its slot (slot p of row r holds chunk
+    // p ^ swz(r)). Offsets relative to the tile's first key are fixed per
+    // thread. Keys at or beyond T: K rows there are masked off by the causal
+    // test; V^T columns there are zeroed in LDS before use (fix_tail).
+    int koff[K_PER_T];
+    int64_t voff[V_PER_T];
 #pragma unroll
-            for (int i = 0; i < K_PER_T; ++i) {
-                const int it = tid + NT * i;
-                rk[i] = ld16(Kg + (int64_t)(s0 + it / KCH) * D + (it % KCH) * VEC);
-            }
+    for (int i = 0; i < K_PER_T; ++i) {
+        const int it = tid + NT * i, r = it / KCH, p = it % KCH;
+        koff[i] = r * D + (p ^ (((r & 3) | (((r >> 3) & 1) << 2)) & (KCH - 1))) * VEC;
+    }
 #pragma unroll
-            for (int i = 0; i < V_PER_T; ++i) {
-                const int it = tid + NT * i;
-                rv[i] = ld16(Vg + (int64_t)(it / VCH) * vrow + s0 + (it % VCH) * VEC);
-            }
-            return;
-        }
-#pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            const int it = tid + NT * i, r = it / KCH, ch = it % KCH;
-            rk[i] = (it < BKV * KCH && s0 + r < T_) ? ld16(Kg + (int64_t)(s0 + r) * D + ch * VEC) : zero;
-        }
-#pragma unroll
-        for (int i = 0; i < V_PER_T; ++i) {
-            const int it = tid + NT * i, r = it / VCH, ch = it % VCH;
-            const int s = s0 + ch * VEC;       // first key of this chunk (in bounds: Tpad pads)
-            u32x4 v = zero;
-            if (it < D * VCH) {
-                v = ld16(Vg + (int64_t)r * vrow + s);
-                if (s + VEC > T_) {             // zero the keys at or beyond T
-                    T* e = reinterpret_cast<T*>(&v);
-#pragma unroll
-                    for (int q = 0; q < VEC; ++q)
-                        if (s + q >= T_) e[q] = from_f32<T>(0.f);
-                }
-            }
-            rv[i] = v;
-        }
-    };
-    auto sstore = [&](int buf) {
-        char* Ks = lds + buf * STAGE;
+    for (int i = 0; i < V_PER_T; ++i) {
+        const int it = tid + NT * i, r = it / VCH, p = it % VCH;
+        voff[i] = (int64_t)r * vrow + (int64_t)(p ^ (r & (VCH - 1))) * VEC;
+    }
+    auto stage_ptr = [&](auto stage) -> char* { return decltype(stage)::value == 0 ? lds_a : lds_b; };
+    auto dma = [&](int j, auto stage) {
+        const int64_t s0 = (int64_t)j * BKV;
+        char* Ks = stage_ptr(stage);
         char* Vs = Ks + K_BYTES;
 #pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            const int it = tid + NT * i;
-            if (K_EXACT || it < BKV * KCH) st16(Ks + k_chunk_off<KCH>(it / KCH, it % KCH), rk[i]);
-        }
+        for (int i = 0; i < K_PER_T; ++i)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kg + s0 * D + koff[i]),
+                                             (__attribute__((address_space(3))) void*)(Ks + (NT * i + 64 * wave) * 16),
+                                             16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < V_PER_T; ++i) {
-            const int it = tid + NT * i;
-            if (V_EXACT || it < D * VCH) st16(Vs + v_chunk_off<VCH>(it / VCH, it % VCH), rv[i]);
+        for (int i = 0; i < V_PER_T; ++i)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vg + s0 + voff[i]),
+                                             (__attribute__((address_space(3))) void*)(Vs + (NT * i + 64 * wave) * 16),
+                                             16, 0, 0);
+    };
+    // Last tile of a sequence: zero the V^T entries of keys >= T (their P is
+    // 0, but padding may hold anything). Call after the tile's barrier; ends
+    // with a barrier.
+    auto fix_tail = [&](int j, auto stage) {
+        const int s0 = j * BKV;
+        if (s0 + BKV <= T_) return;                     // uniform
+        char* Vs = stage_ptr(stage) + K_BYTES;
+        for (int it = tid; it < D * VCH; it += NT) {
+            const int r = it / VCH, c = it % VCH, k0 = s0 + c * VEC;
+            if (k0 + VEC <= T_) continue;
+            T* e = reinterpret_cast<T*>(Vs + v_chunk_off<VCH>(r, c));
+#pragma unroll
+            for (int q = 0; q < VEC; ++q)
+                if (k0 + q >= T_) e[q] = from_f32<T>(0.f);
         }
+        __syncthreads();
     };
 
     // One key tile; the LDS stage is a compile-time constant so every LDS
     // address is a per-lane base plus an immediate offset.
     auto tile = [&](int j, auto stage) {
         constexpr int ST = decltype(stage)::value;
-        if (j + 1 < n_kv) gload(j + 1);
+        fix_tail(j, stage);
+        if (j + 1 < n_kv) dma(j + 1, StageC<ST ^ 1>{});
         const int s0 = j * BKV;
         if (s0 <= t_last) {                    // else every key is above every query of this wave
-            const char* Ks = lds + ST * STAGE;
+            const char* Ks = stage_ptr(stage);
             const char* Vs = Ks + K_BYTES;
             // S^T = K Q^T - m, accumulated from the current reference.
             // The first MFMA of every block takes -m as its C operand.
@@ -435,12 +438,10 @@ void attn_fwd_kernel(AttnArgs a) {
                 }
             }
         }
-        if (j + 1 < n_kv) sstore(ST ^ 1);
-        __syncthreads();
+        __syncthreads();    // releases this stage and (waiting for the loads) publishes the next
     };
 
-    gload(0);
-    sstore(0);
+    dma(0, StageC<0>{});
     __syncthreads();
     for (int j = 0; j < n_kv; j += 2) {
         tile(j, StageC<0>{});

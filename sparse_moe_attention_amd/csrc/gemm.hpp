@@ -7,8 +7,7 @@
 //   * grouped_q_kernel: the sparse Q projection, one (token chunk, expert)
 //     segment per workgroup, rows gathered through the permutation and
 //     scattered back to the dense [token, group, rank, d] layout.
-// Projections are dense contractions, so they run on MFMA: 256 threads as
-// WM x WN waves, each wave a (BM/WM) x (BN/WN) block of 16x16 MFMA tiles;
+// Projections are dense contractions, so they run on MFMA: WM x WN waves, each wave a (BM/WM) x (BN/WN) block of 16x16 MFMA tiles;
 // the K loop stages 128-byte rows of A and B through double-buffered LDS.
 #pragma once
 
@@ -42,14 +41,16 @@ struct TileCfg {
     static constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
     static constexpr int FM = BM / (16 * WM);           // 16x16 blocks per wave, rows
     static constexpr int FN = BN / (16 * WN);           // 16x16 blocks per wave, cols
-    static constexpr int A_PER_THREAD = BM * 8 / 256;   // 16-byte chunks each thread loads
-    static constexpr int B_PER_THREAD = BN * 8 / 256;
+    static constexpr int NTH = WM * WN * 64;            // threads per workgroup
+    static constexpr int RPP = NTH / 8;                  // tile rows loaded per pass (8 chunks a row)
+    static constexpr int A_PER_THREAD = BM * 8 / NTH;   // 16-byte chunks each thread loads
+    static constexpr int B_PER_THREAD = BN * 8 / NTH;
     static constexpr int A_BYTES = BM * kPitch;
     static constexpr int B_BYTES = BN * kPitch;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-    static_assert(WM * WN == 4, "256 threads = 4 waves");
-    static_assert(BM * 8 % 256 == 0 && BN * 8 % 256 == 0, "tile rows must split over 256 threads");
+    static_assert(WM * WN == 4 || WM * WN == 8, "4 or 8 waves");
+    static_assert(BM * 8 % NTH == 0 && BN * 8 % NTH == 0, "tile rows must split over the threads");
 };
 
 // K loop. a_row[i] / b_row[i] point at the tile rows this thread loads
@@ -104,9 +105,9 @@ __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)
         char* As = lds + buf * Cfg::STAGE_BYTES;
         char* Bs = As + Cfg::A_BYTES;
 #pragma unroll
-        for (int i = 0; i < Cfg::A_PER_THREAD; ++i) st16(As + tile_off(tid / 8 + 32 * i, c16), ra[i]);
+        for (int i = 0; i < Cfg::A_PER_THREAD; ++i) st16(As + tile_off(tid / 8 + Cfg::RPP * i, c16), ra[i]);
 #pragma unroll
-        for (int i = 0; i < Cfg::B_PER_THREAD; ++i) st16(Bs + tile_off(tid / 8 + 32 * i, c16), rb[i]);
+        for (int i = 0; i < Cfg::B_PER_THREAD; ++i) st16(Bs + tile_off(tid / 8 + Cfg::RPP * i, c16), rb[i]);
     };
     auto compute = [&](int buf) {
         const char* As = lds + buf * Cfg::STAGE_BYTES;
@@ -219,12 +220,12 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds, int64_t 
     const T* b_row[Cfg::B_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
-        const int64_t r = m0 + tid / 8 + 32 * i;
+        const int64_t r = m0 + tid / 8 + Cfg::RPP * i;
         a_row[i] = (const T*)a.A + (r < a.M_rows ? r : m0) * a.lda + (tid & 7) * Cfg::VEC;
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_THREAD; ++i) {
-        const int vc = n0 + tid / 8 + 32 * i;
+        const int vc = n0 + tid / 8 + Cfg::RPP * i;
         b_row[i] = (const T*)a.seg[0].W + (tid & 7) * Cfg::VEC;   // columns past every block
         for (int s = 0; s < a.n_segs; ++s) {
             const int c = vc - a.seg[s].col_begin;
@@ -389,7 +390,7 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds, int64_t 
 // multiple of 8, so every tile index keeps its XCD), which lets one tile's
 // stores drain while the next tile's K loop runs.
 template <typename T, class Cfg>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_gemm_kernel(ProjArgs a) {
+__global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_gemm_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     const int64_t n = ((a.M_rows + Cfg::BM - 1) / Cfg::BM) * a.n_tiles_n;
     for (int64_t hw = blockIdx.x; hw < n; hw += gridDim.x) proj_tile<T, Cfg>(a, lds, hw);
@@ -425,7 +426,7 @@ struct GroupArgs {
 };
 
 template <typename T, class Cfg>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_q_kernel(GroupArgs a) {
+__global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_q_kernel(GroupArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     __shared__ int32_t s_dst[Cfg::BM];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -440,16 +441,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const T* b_row[Cfg::B_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_THREAD; ++i) {
-        const int jj = tid / 8 + 32 * i;
+        const int jj = tid / 8 + Cfg::RPP * i;
         b_row[i] = (const T*)a.Wq + ((int64_t)e * a.d + (jj < a.d ? jj : 0)) * a.K + (tid & 7) * Cfg::VEC;
     }
     const T* a_row[Cfg::A_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
-        const int r = rb + tid / 8 + 32 * i;
+        const int r = rb + tid / 8 + Cfg::RPP * i;
         a_row[i] = (const T*)a.X + (int64_t)a.perm[r < re ? r : rb] * a.ldx + (tid & 7) * Cfg::VEC;
     }
-    for (int r = tid; r < Cfg::BM; r += 256) s_dst[r] = (rb + r < re) ? a.dst[rb + r] : -1;
+    for (int r = tid; r < Cfg::BM; r += Cfg::NTH) s_dst[r] = (rb + r < re) ? a.dst[rb + r] : -1;
     // Swapped operands: a lane holds output columns c .. c+3 of tile row r.
     f32x4 acc[Cfg::FM][Cfg::FN];
     gemm_mainloop<T, Cfg, true>(lds, a_row, b_row, a.K, acc);   // its barriers publish s_dst

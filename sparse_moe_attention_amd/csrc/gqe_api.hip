@@ -29,7 +29,11 @@ using namespace gqe;
 
 namespace {
 
-using ProjBf16 = TileCfg<bf16, 128, 128, 2, 2>;
+#ifndef GQE_PROJ_BM
+#define GQE_PROJ_BM 128
+#define GQE_PROJ_WM 2
+#endif
+using ProjBf16 = TileCfg<bf16, GQE_PROJ_BM, 128, GQE_PROJ_WM, 2>;
 using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
 using GrpBf16 = TileCfg<bf16, 128, 64, 4, 1>;
 using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
@@ -120,11 +124,12 @@ template <typename T, class Cfg>
 void launch_proj(ProjArgs& a, int total_cols, hipStream_t st) {
     a.n_tiles_n = (total_cols + Cfg::BN - 1) / Cfg::BN;
     const int64_t n_m = (a.M_rows + Cfg::BM - 1) / Cfg::BM;
-    // Two resident workgroups per CU (LDS and register budget), rounded to
+    // Eight resident waves per CU (two per SIMD: the register budget), in
     // whole XCD rounds.
     const int64_t tiles = n_m * a.n_tiles_n;
-    const int64_t grid = std::min<int64_t>(tiles, 2 * (int64_t)align_up((size_t)device_cus(), 8));
-    hipLaunchKernelGGL((proj_gemm_kernel<T, Cfg>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    const int per_cu = 8 / (Cfg::WM * Cfg::WN);
+    const int64_t grid = std::min<int64_t>(tiles, per_cu * (int64_t)align_up((size_t)device_cus(), 8));
+    hipLaunchKernelGGL((proj_gemm_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NTH), 0, st, a);
 }
 
 struct SegList {
@@ -181,8 +186,8 @@ void run_grouped_q(const Dims& d, const void* x, const void* Wq, void* Qr, const
     g.n_t = (int)((d.N + bm - 1) / bm);
     // 8 * E * ceil(n_t / 8) workgroups: tile t = 8*(j/E) + hw%8 of expert j%E, j = hw/8.
     const dim3 grid((unsigned)(8 * (int64_t)d.E * ((g.n_t + 7) / 8)));
-    if (d.f32) hipLaunchKernelGGL((grouped_q_kernel<float, GrpF32>), grid, dim3(256), 0, st, g);
-    else hipLaunchKernelGGL((grouped_q_kernel<bf16, GrpBf16>), grid, dim3(256), 0, st, g);
+    if (d.f32) hipLaunchKernelGGL((grouped_q_kernel<float, GrpF32>), grid, dim3(GrpF32::NTH), 0, st, g);
+    else hipLaunchKernelGGL((grouped_q_kernel<bf16, GrpBf16>), grid, dim3(GrpBf16::NTH), 0, st, g);
 }
 
 void run_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
