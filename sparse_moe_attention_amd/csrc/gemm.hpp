@@ -13,6 +13,11 @@
 
 #include "gqe_common.hpp"
 
+// 1: K loops stage tiles with direct global->LDS loads; 0: through registers.
+#ifndef GQE_GEMM_DMA
+#define GQE_GEMM_DMA 1
+#endif
+
 namespace gqe {
 
 // LDS tile rows are 128 bytes (one K step), unpadded; the eight 16-byte
@@ -48,7 +53,7 @@ struct TileCfg {
     static constexpr int A_BYTES = BM * kPitch;
     static constexpr int B_BYTES = BN * kPitch;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int LDS_BYTES = (GQE_GEMM_DMA ? 1 : 2) * STAGE_BYTES;   // the second DMA stage is its own array
     static_assert(WM * WN == 4 || WM * WN == 8, "4 or 8 waves");
     static_assert(BM * 8 % NTH == 0 && BN * 8 % NTH == 0, "tile rows must split over the threads");
 };
@@ -150,6 +155,101 @@ __device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)
     }
 }
 
+// The same K loop with the tiles staged by gfx950's direct global->LDS loads
+// (global_load_lds_dwordx4): each lane fetches the global chunk that the
+// swizzled layout puts in its LDS slot, so tiles never pass through
+// registers. Stage kt+1 loads while stage kt computes; the two stages are
+// separate LDS arrays, so the compiler does not make the reads of one wait
+// for the loads into the other. A partial last K step zeroes the A chunks at
+// or beyond K in LDS (their B chunks hold finite data from the row start).
+template <typename T, class Cfg, bool SWAP>
+__device__ __forceinline__ void gemm_mainloop_dma(char* lds0, char* lds1, const T* const (&a_row)[Cfg::A_PER_THREAD],
+                                                  const T* const (&b_row)[Cfg::B_PER_THREAD], int K,
+                                                  f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    const int c16 = tid & 7;
+    const int cl = c16 ^ ((tid >> 3) & 7);                // logical chunk of this lane's slot (row & 7 = (tid/8) & 7)
+    const int adj = (cl - c16) * Cfg::VEC;                 // the row pointers point at chunk c16
+    const int nk = (K + Cfg::BK - 1) / Cfg::BK;
+    static_assert(Cfg::RPP % 8 == 0, "slot rows keep their swizzle phase across passes");
+
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto dma = [&](int kt, char* buf) {
+        const bool kin = kt * Cfg::BK + cl * Cfg::VEC < K;
+        const int ko = kin ? kt * Cfg::BK : 0;
+#pragma unroll
+        for (int i = 0; i < Cfg::A_PER_THREAD; ++i)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(a_row[i] + adj + ko),
+                                             (__attribute__((address_space(3))) void*)(buf + (Cfg::NTH * i + 64 * wave) * 16),
+                                             16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < Cfg::B_PER_THREAD; ++i)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(b_row[i] + adj + ko),
+                                             (__attribute__((address_space(3))) void*)(buf + Cfg::A_BYTES +
+                                                                                     (Cfg::NTH * i + 64 * wave) * 16),
+                                             16, 0, 0);
+    };
+    auto fix_k_tail = [&](int kt, char* buf) {
+        if ((kt + 1) * Cfg::BK <= K) return;              // uniform
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (int s = tid; s < Cfg::BM * 8; s += Cfg::NTH) {
+            const int r = s / 8, pc = s % 8;
+            if (kt * Cfg::BK + (pc ^ (r & 7)) * Cfg::VEC >= K) st16(buf + r * kPitch + pc * 16, zero);
+        }
+        __syncthreads();
+    };
+    auto compute = [&](const char* As) {
+        const char* Bs = As + Cfg::A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < Cfg::BK / 32; ++ks) {
+            const int kc = (ks * 32 + 8 * (lane >> 4)) * (int)sizeof(T) / 16;   // 16-byte chunk
+            Frag<T> af[Cfg::FM], bfg[Cfg::FN];
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+                af[i] = ld_tile_frag<T>(As, (wm * Cfg::FM + i) * 16 + (lane & 15), kc);
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j)
+                bfg[j] = ld_tile_frag<T>(Bs, (wn * Cfg::FN + j) * 16 + (lane & 15), kc);
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+                    acc[i][j] = SWAP ? mma16(bfg[j], af[i], acc[i][j]) : mma16(af[i], bfg[j], acc[i][j]);
+        }
+    };
+    auto step = [&](int kt, char* cur, char* nxt) {
+        fix_k_tail(kt, cur);
+        if (kt + 1 < nk) dma(kt + 1, nxt);
+        compute(cur);
+        __syncthreads();   // releases cur and (waiting for the loads) publishes nxt
+    };
+    dma(0, lds0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, lds0, lds1);
+        if (kt + 1 < nk) step(kt + 1, lds1, lds0);
+    }
+}
+
+// Dispatch to the configured K loop; lds0/lds1 are two STAGE_BYTES arrays.
+template <typename T, class Cfg, bool SWAP>
+__device__ __forceinline__ void gemm_kloop(char* lds0, char* lds1, const T* const (&a_row)[Cfg::A_PER_THREAD],
+                                           const T* const (&b_row)[Cfg::B_PER_THREAD], int K,
+                                           f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
+    if constexpr (GQE_GEMM_DMA) {
+        gemm_mainloop_dma<T, Cfg, SWAP>(lds0, lds1, a_row, b_row, K, acc);
+    } else {
+        static_assert(Cfg::STAGE_BYTES % 16 == 0, "stages are contiguous");
+        gemm_mainloop<T, Cfg, SWAP>(lds0, a_row, b_row, K, acc);   // uses lds0[0, 2*STAGE_BYTES)
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Multi-block projection: out_s = A W_s^T for up to 4 weight blocks W_s laid
 // side by side as one virtual weight matrix (block s starts at virtual column
@@ -209,7 +309,7 @@ struct ProjArgs {
 };
 
 template <typename T, class Cfg>
-__device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds, int64_t hw) {
+__device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* lds1, int64_t hw) {
     const int tid = threadIdx.x;
     const int64_t n_m = (a.M_rows + Cfg::BM - 1) / Cfg::BM;
     const int64_t L = xcd_logical_id(hw, n_m * a.n_tiles_n);
@@ -266,7 +366,7 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds, int64_t 
 
     if (trans) {
         // Transposed heads: a lane holds tokens r .. r+3 of column c.
-        gemm_mainloop<T, Cfg, false>(lds, a_row, b_row, a.K, acc);
+        gemm_kloop<T, Cfg, false>(lds0, lds1, a_row, b_row, a.K, acc);
         const int64_t ldo = (int64_t)a.Bt * a.Tpad;
         if (fast) {
             const ProjSeg& sg = a.seg[full_seg];
@@ -313,7 +413,7 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds, int64_t 
     }
 
     // Row-major outputs: a lane holds columns c .. c+3 of row r.
-    gemm_mainloop<T, Cfg, true>(lds, a_row, b_row, a.K, acc);
+    gemm_kloop<T, Cfg, true>(lds0, lds1, a_row, b_row, a.K, acc);
     if (fast) {
         const ProjSeg& sg = a.seg[full_seg];
         const int c0 = n0 - sg.col_begin + wn * Cfg::FN * 16 + 4 * (lane >> 4);
@@ -391,9 +491,12 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds, int64_t 
 // stores drain while the next tile's K loop runs.
 template <typename T, class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_gemm_kernel(ProjArgs a) {
+    // Two LDS stages; with the register-staged K loop they must be contiguous.
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_b[GQE_GEMM_DMA ? Cfg::STAGE_BYTES : 16];
+    char* lds1 = GQE_GEMM_DMA ? lds_b : lds + Cfg::STAGE_BYTES;
     const int64_t n = ((a.M_rows + Cfg::BM - 1) / Cfg::BM) * a.n_tiles_n;
-    for (int64_t hw = blockIdx.x; hw < n; hw += gridDim.x) proj_tile<T, Cfg>(a, lds, hw);
+    for (int64_t hw = blockIdx.x; hw < n; hw += gridDim.x) proj_tile<T, Cfg>(a, lds, lds1, hw);
 }
 
 // ---------------------------------------------------------------------------
@@ -428,6 +531,8 @@ struct GroupArgs {
 template <typename T, class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_q_kernel(GroupArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_b[GQE_GEMM_DMA ? Cfg::STAGE_BYTES : 16];
+    char* lds1 = GQE_GEMM_DMA ? lds_b : lds + Cfg::STAGE_BYTES;
     __shared__ int32_t s_dst[Cfg::BM];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
@@ -453,7 +558,7 @@ __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int r = tid; r < Cfg::BM; r += Cfg::NTH) s_dst[r] = (rb + r < re) ? a.dst[rb + r] : -1;
     // Swapped operands: a lane holds output columns c .. c+3 of tile row r.
     f32x4 acc[Cfg::FM][Cfg::FN];
-    gemm_mainloop<T, Cfg, true>(lds, a_row, b_row, a.K, acc);   // its barriers publish s_dst
+    gemm_kloop<T, Cfg, true>(lds, lds1, a_row, b_row, a.K, acc);   // its barriers publish s_dst
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
         const int drow = s_dst[(wm * Cfg::FM + i) * 16 + (lane & 15)];
