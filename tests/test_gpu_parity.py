@@ -31,6 +31,8 @@ CASES = {
     # 9 regular KV streams and one or two shared-head tiles per level: some
     # levels have more streams homed on an XCD than slots landing on it.
     "many_groups": Shape(B=1, T=300, D=128, G=10, M=4, k=4, d=32),
+    # Wo contracts over (G*k + 2)*d = 96 columns: the GEMM's last K step is partial.
+    "partial_k_step": Shape(B=2, T=230, D=128, G=1, M=2, k=1, d=32, router_bias=True),
 }
 
 # Dense GQA layers (Hq = G*M query heads over G KV groups). 3 sequences x 3
@@ -40,6 +42,8 @@ GQA_CASES = {
     "gqa_9_streams": Shape(B=3, T=600, D=128, G=3, M=2, k=1, d=32),
     "gqa_ragged_f32": Shape(B=2, T=333, D=64, G=1, M=4, k=1, d=64, dtype="f32"),
     "gqa_wide": Shape(B=1, T=515, D=256, G=5, M=3, k=1, d=64),
+    # 3 heads x 32: the output projection contracts over 96 columns (partial last K step).
+    "gqa_partial_k_step": Shape(B=2, T=190, D=64, G=1, M=3, k=1, d=32),
 }
 
 
