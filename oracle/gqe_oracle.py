@@ -30,7 +30,9 @@ Readings where the pages are silent (each is listed in the design doc):
   * the shared head has its own query projection and reads the K/V of group
     shared_kv_group (0 by default);
   * the merged output is [hard slots g-major, rank-minor | weighted | shared],
-    then multiplied by Wo.T.
+    then multiplied by Wo.T;
+  * the ablations' weighted concatenation scales each hard slot by its pick's
+    per-group softmax probability (not renormalised).
 
 All pins live in tests/test_oracle.py; every function here is pinned there.
 """
@@ -41,6 +43,7 @@ import numpy as np
 __all__ = [
     "router_logits", "group_softmax", "select_topk", "renormalize", "route",
     "project", "causal_attention", "weighted_slot", "assemble_slots",
+    "VARIANTS", "variant_slots", "pick_probs", "assemble_variant",
     "gqe_forward", "gqa_forward", "gqe_rows", "gqa_rows", "active_heads",
 ]
 
@@ -155,6 +158,47 @@ def assemble_slots(O: np.ndarray, wsum: np.ndarray, O_sh: np.ndarray) -> np.ndar
     return np.concatenate([O.reshape(N, -1), wsum, O_sh], axis=1)
 
 
+# ----------------------------------------------------------------------------
+# The pages' ablations of the merge. [GQE-n] part 6 compares the full layer
+# with a weighted concatenation that has no renormalised weighted-sum slot
+# (the router's scores weight the expert outputs directly) and with a pure hard
+# concatenation (no weighting at all); [GQE-x] "Experimental results" reports
+# removing the renormalised slot or the shared head. Readings: "the router's
+# scores" are each pick's per-group softmax probability, not renormalised;
+# every variant keeps the other parts of the merge and the slot order.
+# ----------------------------------------------------------------------------
+VARIANTS = ("full", "weighted_concat", "hard_concat", "no_shared")
+
+
+def variant_slots(G: int, k: int, variant: str = "full") -> int:
+    """d-wide slots of the merged output: G*k hard slots plus the weighted and
+    shared slots that the variant keeps."""
+    return G * k + (2 if variant == "full" else 1)
+
+
+def pick_probs(p: np.ndarray, sel: np.ndarray) -> np.ndarray:
+    """p_pick[n,g,r] = p[n, g, sel[n,g,r]]: the router probability of each pick."""
+    return np.take_along_axis(p, sel, axis=2)
+
+
+def assemble_variant(O: np.ndarray, w: np.ndarray, p_pick: np.ndarray, O_sh, variant: str) -> np.ndarray:
+    """Merged slots of each variant (O [N,G,k,d], w and p_pick [N,G,k], O_sh [N,d]):
+      full             [O | sum w O | O_sh]
+      weighted_concat  [p_pick * O | O_sh]
+      hard_concat      [O | O_sh]
+      no_shared        [O | sum w O]"""
+    N = O.shape[0]
+    if variant == "full":
+        return assemble_slots(O, weighted_slot(O, w), O_sh)
+    if variant == "weighted_concat":
+        return np.concatenate([(O * p_pick[..., None]).reshape(N, -1), O_sh], axis=1)
+    if variant == "hard_concat":
+        return np.concatenate([O.reshape(N, -1), O_sh], axis=1)
+    if variant == "no_shared":
+        return np.concatenate([O.reshape(N, -1), weighted_slot(O, w)], axis=1)
+    raise ValueError(f"unknown variant {variant!r}")
+
+
 def _routed_queries(x: np.ndarray, Wq: np.ndarray, sel: np.ndarray) -> np.ndarray:
     """Qr[n,g,r] = x[n] . Wq[g, sel[n,g,r]].T, computed expert by expert over the
     tokens that picked it (no query is formed for an expert a token skipped).
@@ -172,11 +216,13 @@ def _routed_queries(x: np.ndarray, Wq: np.ndarray, sel: np.ndarray) -> np.ndarra
 
 
 def gqe_forward(inp: dict, G: int, M: int, k: int, d: int, B: int, T: int,
-                shared_kv_group: int = 0, q_block: int = 512) -> dict:
+                shared_kv_group: int = 0, q_block: int = 512, variant: str = "full") -> dict:
     """The whole GQE layer in fp64. inp holds float64 arrays x, Wr, br (or None),
-    Wq [G*M*d,D], Wk [G*d,D], Wv [G*d,D], Wq_sh [d,D], Wo [D,(G*k+2)*d].
+    Wq [G*M*d,D], Wk [G*d,D], Wv [G*d,D], Wq_sh [d,D], Wo [D, variant_slots*d].
 
-    Expert e = g*M + m owns rows e*d .. e*d+d-1 of Wq.
+    Expert e = g*M + m owns rows e*d .. e*d+d-1 of Wq. The returned w is the
+    weight the variant applies to each pick: p_pick for the weighted
+    concatenation, the renormalised w otherwise.
     """
     x = inp["x"]
     N = x.shape[0]
@@ -196,13 +242,15 @@ def gqe_forward(inp: dict, G: int, M: int, k: int, d: int, B: int, T: int,
             q = Qr[:, g, r].reshape(B, T, d)
             O[:, g, r] = causal_attention(q, K[:, :, g], V[:, :, g], q_block).reshape(N, d)
     s0 = shared_kv_group
-    O_sh = causal_attention(Q_sh.reshape(B, T, d), K[:, :, s0], V[:, :, s0], q_block).reshape(N, d)
+    O_sh = None
+    if variant != "no_shared":
+        O_sh = causal_attention(Q_sh.reshape(B, T, d), K[:, :, s0], V[:, :, s0], q_block).reshape(N, d)
 
-    wsum = weighted_slot(O, w)
-    C = assemble_slots(O, wsum, O_sh)
+    p_pick = pick_probs(p, sel)
+    C = assemble_variant(O, w, p_pick, O_sh, variant)
     out = project(C, inp["Wo"])
-    return dict(logits=logits, p=p, idx=sel, w=w, Qr=Qr, Q_sh=Q_sh,
-                K=K.reshape(N, G, d), V=V.reshape(N, G, d), C=C, out=out)
+    return dict(logits=logits, p=p, idx=sel, w=(p_pick if variant == "weighted_concat" else w), Qr=Qr,
+                Q_sh=Q_sh, K=K.reshape(N, G, d), V=V.reshape(N, G, d), C=C, out=out)
 
 
 def gqa_forward(inp: dict, G: int, Hq: int, d: int, B: int, T: int, q_block: int = 512) -> dict:
@@ -274,7 +322,7 @@ def _rows_attention(x, heads, Wk, Wv, G, d, B, T, rows, kv_chunk):
 
 
 def gqe_rows(inp: dict, G: int, M: int, k: int, d: int, B: int, T: int, rows,
-             shared_kv_group: int = 0, kv_chunk: int = 65536) -> dict:
+             shared_kv_group: int = 0, kv_chunk: int = 65536, variant: str = "full") -> dict:
     """Routing for every token; slots C and out only for the given rows."""
     rows = np.asarray(rows, dtype=np.int64)
     x = inp["x"]
@@ -289,9 +337,10 @@ def gqe_rows(inp: dict, G: int, M: int, k: int, d: int, B: int, T: int, rows,
     grp[G * k] = shared_kv_group
     O_all = _rows_attention(x, (q, grp), inp["Wk"], inp["Wv"], G, d, B, T, rows, kv_chunk)
     O = O_all[:, :G * k].reshape(len(rows), G, k, d)
-    wsum = weighted_slot(O, w[rows])
-    C = assemble_slots(O, wsum, O_all[:, G * k])
-    return dict(logits=logits, p=p, idx=sel, w=w, rows=rows, C=C, out=project(C, inp["Wo"]))
+    p_pick = pick_probs(p, sel)
+    C = assemble_variant(O, w[rows], p_pick[rows], O_all[:, G * k], variant)
+    return dict(logits=logits, p=p, idx=sel, w=(p_pick if variant == "weighted_concat" else w), rows=rows,
+                C=C, out=project(C, inp["Wo"]))
 
 
 def gqa_rows(inp: dict, G: int, Hq: int, d: int, B: int, T: int, rows, kv_chunk: int = 65536) -> dict:

@@ -352,6 +352,43 @@ def pin_rows_mode():
     assert np.allclose(gp["out"], gf["out"][rows], rtol=0, atol=1e-12)
 
 
+def pin_variants_against_full():
+    """The ablations' merges against the full layer's slots: hard concat and
+    no-shared are the full merge with one slot dropped; the weighted concat's
+    scaled hard slots, summed and divided by the sum of the pick probabilities,
+    give the full layer's renormalised weighted slot; the no-shared variant
+    never reads Wq_sh."""
+    rng = np.random.default_rng(23)
+    B, T, D, G, M, k, d = 2, 33, 32, 3, 3, 2, 8
+    inp = rand_layer(rng, B, T, D, G, M, k, d, bias=True)
+    GK, N = G * k, B * T
+    full = _layer(inp, B, T, G, M, k, d)
+    for variant in ("weighted_concat", "hard_concat", "no_shared"):
+        Wo = inp["Wo"][:, :go.variant_slots(G, k, variant) * d]
+        v = go.gqe_forward(dict(inp, Wo=Wo), G, M, k, d, B, T, q_block=16, variant=variant)
+        assert v["C"].shape == (N, (GK + 1) * d)
+        assert np.allclose(v["out"], v["C"] @ Wo.T, rtol=0, atol=1e-12)
+        hard = full["C"][:, :GK * d]
+        if variant == "hard_concat":
+            assert np.array_equal(v["C"], np.concatenate([hard, full["C"][:, (GK + 1) * d:]], axis=1))
+        if variant == "no_shared":
+            assert np.array_equal(v["C"], full["C"][:, :(GK + 1) * d])
+            nosh = go.gqe_forward(dict(inp, Wo=Wo, Wq_sh=np.full_like(inp["Wq_sh"], np.nan)), G, M, k, d, B, T,
+                                  q_block=16, variant=variant)
+            assert np.array_equal(nosh["out"], v["out"])
+        if variant == "weighted_concat":
+            pp = v["w"]                                           # per-group probabilities of the picks
+            assert np.allclose(pp, np.take_along_axis(full["p"], full["idx"], axis=2), rtol=0, atol=0)
+            scaled = v["C"][:, :GK * d].reshape(N, GK, d)
+            wsum = scaled.sum(axis=1) / pp.reshape(N, GK).sum(axis=1, keepdims=True)
+            assert np.allclose(wsum, full["C"][:, GK * d:(GK + 1) * d], rtol=1e-12, atol=1e-14)
+            assert np.array_equal(v["C"][:, GK * d:], full["C"][:, (GK + 1) * d:])
+            # each slot is its hard slot times one probability in (0, 1]
+            ratio = scaled / hard.reshape(N, GK, d)
+            assert np.allclose(ratio, pp.reshape(N, GK, 1), rtol=1e-12)
+            assert (pp > 0).all() and (pp <= 1).all()
+
+
 PINS = [
     pin_topk_brute_force, pin_group_softmax_scipy, pin_route_tiny_brute_force,
     pin_route_uniform_router, pin_route_single_expert, pin_route_invariants,
@@ -359,7 +396,7 @@ PINS = [
     pin_layer_causality, pin_layer_batch_independence, pin_reduction_to_gqa,
     pin_gqa_vs_sdpa_endpoints, pin_slots_closed_form, pin_hard_slot_rank_order,
     pin_expert_permutation_invariance, pin_linearity_in_Wo, pin_active_heads_pages,
-    pin_rows_mode,
+    pin_rows_mode, pin_variants_against_full,
 ]
 
 
@@ -430,6 +467,18 @@ def _weighted_slot_unweighted(O, w):
     return O.mean(axis=(1, 2))
 
 
+_orig_assemble_variant = go.assemble_variant
+
+
+def _assemble_variant_renormalised(O, w, p_pick, O_sh, variant):
+    """Weighted concatenation that scales by the renormalised w instead of p."""
+    return _orig_assemble_variant(O, w, w if variant == "weighted_concat" else p_pick, O_sh, variant)
+
+
+def _pick_probs_rank_shifted(p, sel):
+    return np.take_along_axis(p, np.roll(sel, 1, axis=2), axis=2)
+
+
 MUTANTS = {
     "topk_ties_to_high_index": ("select_topk", _topk_ties_high),
     "renormalise_per_group": ("renormalize", _renorm_per_group),
@@ -440,6 +489,8 @@ MUTANTS = {
     "weighted_and_shared_swapped": ("assemble_slots", _assemble_swapped),
     "hard_slots_in_reverse_rank": ("assemble_slots", _assemble_rank_reversed),
     "weighted_slot_ignores_w": ("weighted_slot", _weighted_slot_unweighted),
+    "weighted_concat_uses_renormalised_w": ("assemble_variant", _assemble_variant_renormalised),
+    "pick_probabilities_of_wrong_rank": ("pick_probs", _pick_probs_rank_shifted),
 }
 
 
