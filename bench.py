@@ -14,6 +14,7 @@ oracle timed on the host's cores (a baseline only).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -37,10 +38,15 @@ def attn_flops(s, heads: int) -> float:
     return heads * s.B * 4.0 * s.d * s.T * (s.T + 1) / 2.0
 
 
+def active_heads(s) -> int:
+    """Attention heads per token: the routed picks plus the shared head unless the merge drops it."""
+    return s.G * s.k + (0 if getattr(s, "variant", "full") == "no_shared" else 1)
+
+
 def layer_flops(s) -> float:
-    per_tok = (2 * s.D * s.G * s.M + 2 * s.D * (s.G * s.k + 1) * s.d + 4 * s.D * s.G * s.d
-               + 2 * (s.G * s.k + 2) * s.d * s.D + 2 * s.G * s.k * s.d)
-    return s.N * per_tok + attn_flops(s, s.G * s.k + 1)
+    per_tok = (2 * s.D * s.G * s.M + 2 * s.D * active_heads(s) * s.d + 4 * s.D * s.G * s.d
+               + 2 * s.slots * s.d * s.D + 2 * s.G * s.k * s.d)
+    return s.N * per_tok + attn_flops(s, active_heads(s))
 
 
 def source_sha(path: str) -> str:
@@ -85,12 +91,12 @@ def cpu_baseline(s, inp, target_s: float):
     # calibrate the row count on a small sample, then fill the time budget
     r0 = 16
     t = time.perf_counter()
-    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, sample_rows(s, r0, 7))
+    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, sample_rows(s, r0, 7), variant=s.variant)
     per_row = max((time.perf_counter() - t - t_fixed) / r0, 1e-6)
     R = int(min(s.N, max(r0, (target_s - t_fixed) / per_row)))
     rows = sample_rows(s, R, 11)
     t = time.perf_counter()
-    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, rows)
+    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, rows, variant=s.variant)
     t_rows = time.perf_counter() - t
     per_row = max((t_rows - t_fixed) / len(rows), 1e-9)
     est = t_fixed + s.N * per_row
@@ -112,6 +118,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gqa", action="store_true")
+    ap.add_argument("--variant", default="full", choices=["full", "weighted_concat", "hard_concat", "no_shared"],
+                    help="merge of the picked experts: the layer, or one of the pages' ablations")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the reference that scales "
                          "rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -138,6 +146,10 @@ def main():
     gq.load()
     torch.cuda.set_device(0)
     s, inp = config_inputs(args.config)
+    if args.variant != "full":
+        # the ablations' Wo has one slot fewer; its leading columns serve
+        s = dataclasses.replace(s, variant=args.variant)
+        inp = dict(inp, Wo=inp["Wo"][:, :s.slots * s.d].contiguous())
     steps = args.steps if args.steps is not None else {1: 50, 2: 50, 3: 20, 4: 20, 5: 3}[args.config]
     dv = {k: (v.cuda().contiguous() if v is not None else None) for k, v in inp.items()}
     dt = s.torch_dtype()
@@ -214,7 +226,7 @@ def main():
                "attention_speedup": gqa_attn_ms / attn_ms}
 
     peak = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
-    fl = attn_flops(s, s.G * s.k + 1)
+    fl = attn_flops(s, active_heads(s))
     achieved = fl / (attn_ms / 1e3) / 1e12
     traffic = measured_traffic(args.config)
     rec = {
@@ -230,8 +242,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if s.dtype == "bf16" else "f32",
         "data": "synthetic (seeded randn inputs and random-init weights of the layer's shape)",
-        "config": {"workload": CONFIG_NAMES[args.config], "B": s.B, "T": s.T, "D": s.D, "G": s.G, "M": s.M,
-                   "k": s.k, "d_h": s.d, "shared_kv_group": s.shared_kv_group, "tokens_per_step": s.N},
+        "config": {"workload": CONFIG_NAMES[args.config] + ("" if s.variant == "full" else f", {s.variant} merge"),
+                   "B": s.B, "T": s.T, "D": s.D, "G": s.G, "M": s.M, "k": s.k, "d_h": s.d,
+                   "shared_kv_group": s.shared_kv_group, "variant": s.variant, "tokens_per_step": s.N},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
                      "algorithmic_flops_per_launch": fl, "avg_launch_ms": attn_ms},

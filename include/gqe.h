@@ -78,10 +78,28 @@ typedef enum { GQE_BF16 = 0, GQE_F32 = 1 } gqe_dtype;
  * M query experts per group, k experts picked per group, d_h head width,
  * shared_kv_group the KV group the always-on shared head reads,
  * dtype a gqe_dtype. */
+/* How the picked experts' outputs are merged before the output projection.
+ * GQE_FULL is the layer; the others are the ablations the FrontiersMind GQE
+ * article compares in part 6 (and the explainer's "Experimental results"):
+ *   GQE_FULL             C = [hard slots | sum_s w_s O_s | shared]   (G*k+2 slots)
+ *   GQE_WEIGHTED_CONCAT  C = [p_s O_s per hard slot | shared]        (G*k+1 slots)
+ *                        p_s = the pick's per-group router probability, not
+ *                        renormalised (what gqe_route then returns as w)
+ *   GQE_HARD_CONCAT      C = [hard slots | shared]                   (G*k+1 slots)
+ *   GQE_NO_SHARED        C = [hard slots | sum_s w_s O_s]            (G*k+1 slots)
+ * Wo is [D, slots*d_h] with the variant's slot count. */
+typedef enum {
+    GQE_FULL = 0,
+    GQE_WEIGHTED_CONCAT = 1,
+    GQE_HARD_CONCAT = 2,
+    GQE_NO_SHARED = 3
+} gqe_variant;
+
 typedef struct {
     int64_t B, T, D;
     int32_t G, M, k, d_h, shared_kv_group;
     int32_t dtype;
+    int32_t variant;   /* gqe_variant; GQE_FULL for the layer itself */
 } gqe_shape;
 
 /* Bytes of device workspace gqe_route, gqe_attn_fwd_routed and gqe_attn_fwd
@@ -95,7 +113,8 @@ size_t gqe_workspace_bytes(const gqe_shape* s);
  *   Wr     [G*M, D]            router weight
  *   br     [G*M] fp32 or NULL  per-expert logit offset
  *   idx    [B*T, G, k] int32   out: picked expert m of group g, rank r (best first)
- *   w      [B*T, G, k] fp32    out: renormalised routing weights
+ *   w      [B*T, G, k] fp32    out: renormalised routing weights (the picks' own
+ *                              probabilities for GQE_WEIGHTED_CONCAT)
  *   logits [B*T, G*M] fp32     out (NULL to skip): x Wr^T + br
  *   counts [G*M] int32         out (NULL to skip): tokens routed to each expert
  *   ws, ws_bytes               workspace of at least gqe_workspace_bytes(s) */
@@ -112,16 +131,19 @@ gqe_status gqe_route(const gqe_shape* s, const void* x, const void* Wr, const fl
  *   Wq      [G*M*d_h, D]          query projection of every expert
  *   Wk, Wv  [G*d_h, D]            key and value projections of every group
  *   Wq_sh   [d_h, D]              query projection of the shared head
- *   Wo      [D, (G*k+2)*d_h]      output projection over the merged slots
+ *   Wo      [D, slots*d_h]        output projection over the merged slots (slots:
+ *                                 G*k+2 for GQE_FULL, G*k+1 for the ablations)
  *   idx     [B*T, G, k] int32     picked experts, each in [0, M), distinct
  *                                 within a group; an entry outside [0, M), or
  *                                 repeating an earlier rank's expert in its
  *                                 group, is skipped and its hard slot holds
  *                                 unspecified values (no out-of-bounds access
  *                                 results)
- *   w       [B*T, G, k] fp32      weights of the weighted slot
+ *   w       [B*T, G, k] fp32      weights of the weighted slot (GQE_WEIGHTED_CONCAT:
+ *                                 the factors of the hard slots; GQE_HARD_CONCAT:
+ *                                 unused)
  *   out     [B*T, D]              out: layer output
- *   slots_out [B*T, (G*k+2)*d_h]  out (NULL to skip): the merged slots */
+ *   slots_out [B*T, slots*d_h]    out (NULL to skip): the merged slots */
 gqe_status gqe_attn_fwd_routed(const gqe_shape* s, const void* x, const void* Wq, const void* Wk,
                                const void* Wv, const void* Wq_sh, const void* Wo,
                                const int32_t* idx, const float* w, void* out, void* slots_out,

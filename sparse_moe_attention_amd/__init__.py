@@ -22,6 +22,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgqe.so")
 
 GQE_BF16, GQE_F32 = 0, 1
+# Merge variants (gqe_variant): the layer and the pages' three ablations.
+GQE_FULL, GQE_WEIGHTED_CONCAT, GQE_HARD_CONCAT, GQE_NO_SHARED = 0, 1, 2, 3
+VARIANT_CODES = {"full": GQE_FULL, "weighted_concat": GQE_WEIGHTED_CONCAT, "hard_concat": GQE_HARD_CONCAT,
+                 "no_shared": GQE_NO_SHARED}
 GQE_N_STAGES, GQA_N_STAGES = 8, 3
 GQE_STAGE_NAMES = ("proj_kv_qsh_router", "route", "scan", "scatter", "grouped_q", "attention",
                    "weighted_slot", "out_proj")
@@ -39,6 +43,7 @@ class GqeShape(ctypes.Structure):
         ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
         ("G", ctypes.c_int32), ("M", ctypes.c_int32), ("k", ctypes.c_int32),
         ("d_h", ctypes.c_int32), ("shared_kv_group", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("variant", ctypes.c_int32),
     ]
 
 
@@ -94,15 +99,17 @@ def _check(code: int) -> None:
         raise GqeError(code, gqe_status_str(code))
 
 
-def make_shape(B, T, D, G, M, k, d_h, shared_kv_group=0, dtype=GQE_BF16) -> GqeShape:
-    return GqeShape(B, T, D, G, M, k, d_h, shared_kv_group, dtype)
+def make_shape(B, T, D, G, M, k, d_h, shared_kv_group=0, dtype=GQE_BF16, variant=GQE_FULL) -> GqeShape:
+    return GqeShape(B, T, D, G, M, k, d_h, shared_kv_group, dtype, variant)
 
 
 def shape_from(s) -> GqeShape:
     """GqeShape from any object with B, T, D, G, M, k, d (and optional dtype
     "bf16"/"f32", shared_kv_group) attributes."""
     dt = GQE_F32 if getattr(s, "dtype", "bf16") in ("f32", GQE_F32) else GQE_BF16
-    return make_shape(s.B, s.T, s.D, s.G, s.M, s.k, s.d, getattr(s, "shared_kv_group", 0), dt)
+    v = getattr(s, "variant", GQE_FULL)
+    v = VARIANT_CODES[v] if isinstance(v, str) else int(v)
+    return make_shape(s.B, s.T, s.D, s.G, s.M, s.k, s.d, getattr(s, "shared_kv_group", 0), dt, v)
 
 
 def _ptr(t):

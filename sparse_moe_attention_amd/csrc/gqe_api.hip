@@ -48,8 +48,12 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 struct Dims {
     int64_t B, T, D, N, Tpad, nC;
     int G, M, k, d, E, GK, s0;
+    int variant;       // gqe_variant
+    int slots;         // d-wide slots of the merged output C (Wo's input)
     int esz;
     bool f32;
+    bool weighted_slot() const { return variant == GQE_FULL || variant == GQE_NO_SHARED; }
+    bool shared_head() const { return variant != GQE_NO_SHARED; }
 };
 
 // Shape checks shared by every GQE entry point (no HIP call).
@@ -59,19 +63,22 @@ gqe_status check_shape(const gqe_shape* s, Dims* o) {
     if (s->k > s->M) return GQE_ERR_SHAPE;
     if (s->shared_kv_group < 0 || s->shared_kv_group >= s->G) return GQE_ERR_SHAPE;
     if (s->dtype != GQE_BF16 && s->dtype != GQE_F32) return GQE_ERR_UNSUPPORTED;
+    if (s->variant < GQE_FULL || s->variant > GQE_NO_SHARED) return GQE_ERR_UNSUPPORTED;
     if (s->d_h != 32 && s->d_h != 64) return GQE_ERR_UNSUPPORTED;
     if (s->D % 64 != 0 || s->D > (int64_t)1 << 20) return GQE_ERR_UNSUPPORTED;
     if (s->M > 64 || (int64_t)s->G * s->M > 256) return GQE_ERR_UNSUPPORTED;
     if (s->B > ((int64_t)1 << 31) || s->T > ((int64_t)1 << 31)) return GQE_ERR_SHAPE;
     const int64_t N = s->B * s->T;
     const int64_t GK = (int64_t)s->G * s->k;
-    if (N * (GK + 2) >= ((int64_t)1 << 31)) return GQE_ERR_SHAPE;   // int32 rows of Qr / perm
+    const int slots = (int)GK + (s->variant == GQE_FULL ? 2 : 1);
+    if (N * slots >= ((int64_t)1 << 31)) return GQE_ERR_SHAPE;   // int32 rows of Qr / perm
     Dims d;
     d.B = s->B; d.T = s->T; d.D = s->D; d.N = N;
     d.Tpad = (int64_t)align_up((size_t)s->T, kKVPad);
     d.nC = (N + kChunk - 1) / kChunk;
     d.G = s->G; d.M = s->M; d.k = s->k; d.d = s->d_h;
     d.E = s->G * s->M; d.GK = (int)GK; d.s0 = s->shared_kv_group;
+    d.variant = s->variant; d.slots = slots;
     d.f32 = s->dtype == GQE_F32;
     d.esz = d.f32 ? 4 : 2;
     *o = d;
@@ -98,7 +105,7 @@ GqeWs gqe_layout(const Dims& d) {
     L.Vt = take((size_t)d.G * d.B * d.Tpad * d.d * d.esz);
     L.Qsh = take((size_t)d.N * d.d * d.esz);
     L.Qr = take((size_t)d.N * d.GK * d.d * d.esz);
-    L.C = take((size_t)d.N * (d.GK + 2) * d.d * d.esz);
+    L.C = take((size_t)d.N * d.slots * d.d * d.esz);
     L.total = o;
     return L;
 }
@@ -209,12 +216,21 @@ void run_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
     }
 }
 
+// The merge step of the variant: the renormalised weighted slot (full,
+// no-shared), the hard slots scaled in place by their weights (weighted
+// concatenation), or nothing (hard concatenation).
 void run_combine(const Dims& d, void* C, const float* w, hipStream_t st) {
-    const int64_t ldc = (int64_t)(d.GK + 2) * d.d;
+    if (d.variant == GQE_HARD_CONCAT) return;
+    const int64_t ldc = (int64_t)d.slots * d.d;
+    const int scale_in_place = d.variant == GQE_WEIGHTED_CONCAT;
     const int64_t items = d.N * (d.d / 8);
     const dim3 grid((unsigned)((items + 255) / 256));
-    if (d.f32) hipLaunchKernelGGL((combine_kernel<float>), grid, dim3(256), 0, st, (float*)C, w, d.N, ldc, d.GK, d.d);
-    else hipLaunchKernelGGL((combine_kernel<bf16>), grid, dim3(256), 0, st, (bf16*)C, w, d.N, ldc, d.GK, d.d);
+    if (d.f32)
+        hipLaunchKernelGGL((combine_kernel<float>), grid, dim3(256), 0, st, (float*)C, w, d.N, ldc, d.GK, d.d,
+                           scale_in_place);
+    else
+        hipLaunchKernelGGL((combine_kernel<bf16>), grid, dim3(256), 0, st, (bf16*)C, w, d.N, ldc, d.GK, d.d,
+                           scale_in_place);
 }
 
 gqe_status last_hip() { return hipGetLastError() == hipSuccess ? GQE_OK : GQE_ERR_HIP; }
@@ -238,7 +254,7 @@ gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* 
     if (project_kv) {
         SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
         sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
-        sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
+        if (d.shared_head()) sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
         sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
         run_proj(d, sl, st);
     }
@@ -256,21 +272,21 @@ gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* 
     std::memset(&a, 0, sizeof(a));
     a.Q0 = at(ws, L.Qr);
     a.q0_ld = (int64_t)d.GK * d.d;
-    a.Q1 = at(ws, L.Qsh);
+    a.Q1 = d.shared_head() ? at(ws, L.Qsh) : nullptr;
     a.q1_ld = d.d;
     a.K = at(ws, L.K);
     a.Vt = at(ws, L.Vt);
     a.O = C;
-    a.o_ld = (int64_t)(d.GK + 2) * d.d;
+    a.o_ld = (int64_t)d.slots * d.d;
     a.R = d.k;                 // routed head j = g*k + r: hard slot j of C
     a.kv1 = d.s0;
-    a.o1_col = (d.GK + 1) * d.d;
+    a.o1_col = (d.GK + (d.weighted_slot() ? 1 : 0)) * d.d;   // the shared slot is the last one
     mk.at(5);
     run_attention(d, a, st);
     mk.at(6);
     run_combine(d, C, w, st);
     mk.at(7);
-    SegList so = proj_base(d, C, (int64_t)(d.GK + 2) * d.d, d.N, (d.GK + 2) * d.d);
+    SegList so = proj_base(d, C, (int64_t)d.slots * d.d, d.N, d.slots * d.d);
     so.add(Wo, (int)d.D, out, OUT_ROWS, d.D, nullptr);
     run_proj(d, so, st);
     mk.at(8);
@@ -305,7 +321,7 @@ gqe_status gqe_route(const gqe_shape* s, const void* x, const void* Wr, const fl
     run_proj(d, sl, st);
     int32_t* hist = (int32_t*)at(ws, L.hist);
     hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)lg, idx, w, hist,
-                       d.N, d.G, d.M, d.k);
+                       d.N, d.G, d.M, d.k, (int)(d.variant != GQE_WEIGHTED_CONCAT));
     if (counts)
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, (const int32_t*)hist,
                            (int32_t*)at(ws, L.cbase), (int32_t*)at(ws, L.offsets), counts, (int)d.nC, d.E);
@@ -328,7 +344,7 @@ gqe_status gqe_attn_fwd_routed(const gqe_shape* s, const void* x, const void* Wq
     if (ws_bytes < L.total) return GQE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL((route_kernel<1>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)nullptr,
-                       const_cast<int32_t*>(idx), (float*)nullptr, (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k);
+                       const_cast<int32_t*>(idx), (float*)nullptr, (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k, 1);
     void* C = slots_out ? slots_out : at(ws, L.C);
     return run_post_router(d, L, ws, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, C, st, true, Marks{nullptr, st});
 }
@@ -356,13 +372,13 @@ gqe_status gqe_attn_fwd_timed(const gqe_shape* s, const void* x, const void* Wr,
     // One pass over x: K, V^T, Q_sh and the router logits.
     SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
     sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
-    sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
+    if (d.shared_head()) sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
     sl.add(Wr, d.E, lg, OUT_ROWS_F32, d.E, br);
     sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
     run_proj(d, sl, st);
     mk.at(1);
     hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)lg, idx, w,
-                       (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k);
+                       (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k, (int)(d.variant != GQE_WEIGHTED_CONCAT));
     return run_post_router(d, L, ws, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, at(ws, L.C), st, false, mk);
 }
 

@@ -6,7 +6,8 @@
 // part 4: a light router scores every expert of every group and activates the
 // best k, from the highest score down). Per token and group: softmax of the M
 // logits in fp32, top-k by descending logit with ties to the lower index, and
-// weights p_pick / (sum of p over all G*k picks of the token).
+// weights p_pick / (sum of p over all G*k picks of the token) -- or p_pick
+// itself for the article's weighted-concatenation ablation (part 6).
 //
 // The permutation groups the (token, group, rank) picks by expert e = g*M + m
 // so the sparse Q projection runs as one GEMM per expert segment. It is a
@@ -24,12 +25,13 @@ namespace gqe {
 
 constexpr int kChunk = 256;   // tokens per routing chunk (= workgroup size)
 
-// MODE 0: route from fp32 logits [N, G*M] -> idx, w and the histogram.
+// MODE 0: route from fp32 logits [N, G*M] -> idx, w and the histogram
+// (renorm = 0: w is the pick's probability, not renormalised).
 // MODE 1: histogram of a caller-given idx (entries outside [0, M), and repeats
 // of an earlier rank's expert in the same group, are skipped).
 template <int MODE>
 __global__ __launch_bounds__(256) void route_kernel(const float* logits, int32_t* idx, float* w,
-                                                    int32_t* hist, int64_t N, int G, int M, int k) {
+                                                    int32_t* hist, int64_t N, int G, int M, int k, int renorm) {
     __shared__ int32_t h_lds[256];
     const int E = G * M;
     for (int e = threadIdx.x; e < E; e += 256) h_lds[e] = 0;
@@ -68,8 +70,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* logits, int32_t
                     atomicAdd(&h_lds[g * M + best], 1);
                 }
             }
-            const float inv = 1.f / total;
-            for (int q = 0; q < GK; ++q) wrow[q] = wrow[q] * inv;
+            if (renorm) {
+                const float inv = 1.f / total;
+                for (int q = 0; q < GK; ++q) wrow[q] = wrow[q] * inv;
+            }
         } else {
             for (int g = 0; g < G; ++g)
                 for (int r = 0; r < k; ++r) {
@@ -178,25 +182,33 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* idx, const 
 }
 
 // Weighted slot: C[n, GK*d + c] = sum_s w[n, s] * C[n, s*d + c] over the GK
-// hard slots (fp32 accumulation). One thread per 8 columns of one token.
+// hard slots (fp32 accumulation). With scale_in_place (the weighted
+// concatenation ablation) each hard slot is instead replaced by
+// w[n, s] * C[n, s*d + c]. One thread per 8 columns of one token.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(T* C, const float* w, int64_t N, int64_t ldc, int GK,
-                                                      int d) {
+                                                      int d, int scale_in_place) {
     const int chunks = d / 8;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= N * chunks) return;
     const int64_t n = i / chunks;
     const int c = (int)(i % chunks) * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const T* row = C + n * ldc;
+    T* row = C + n * ldc;
     for (int s = 0; s < GK; ++s) {
         const float ws = w[n * GK + s];
         float v[8];
         load8<T>(row + s * d + c, v);
+        if (scale_in_place) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= ws;
+            store8<T>(row + s * d + c, v);
+            continue;
+        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] += ws * v[q];
     }
-    store8<T>(C + n * ldc + (int64_t)GK * d + c, acc);
+    if (!scale_in_place) store8<T>(row + (int64_t)GK * d + c, acc);
 }
 
 }  // namespace gqe

@@ -29,13 +29,14 @@ def f64_inputs(inp: dict) -> dict:
 
 
 def oracle_routing(f: dict, s: Shape, chunk: int = 65536):
-    """Oracle routing of every token, in token chunks (routing is per token)."""
+    """Oracle routing of every token, in token chunks (routing is per token).
+    w is the weight the shape's merge variant applies to each pick."""
     logits, sel, w = [], [], []
     for n0 in range(0, s.N, chunk):
-        lg, _, se, ww = go.route(f["x"][n0:n0 + chunk], f["Wr"], f.get("br"), s.G, s.M, s.k)
+        lg, p, se, ww = go.route(f["x"][n0:n0 + chunk], f["Wr"], f.get("br"), s.G, s.M, s.k)
         logits.append(lg)
         sel.append(se)
-        w.append(ww)
+        w.append(go.pick_probs(p, se) if s.variant == "weighted_concat" else ww)
     return np.concatenate(logits), np.concatenate(sel), np.concatenate(w)
 
 

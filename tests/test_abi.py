@@ -53,7 +53,7 @@ def test_status_strings(lib):
     (dict(k=3), -2), (dict(k=0), -2), (dict(B=0), -2), (dict(T=0), -2), (dict(G=0), -2),
     (dict(shared_kv_group=2), -2), (dict(shared_kv_group=-1), -2),
     (dict(d_h=48), -3), (dict(D=100), -3), (dict(dtype=7), -3), (dict(M=65, k=1), -3),
-    (dict(G=17, M=16), -3), (dict(B=1 << 20, T=1 << 20), -2),
+    (dict(G=17, M=16), -3), (dict(B=1 << 20, T=1 << 20), -2), (dict(variant=4), -3), (dict(variant=-1), -3),
 ])
 def test_shape_errors(lib, kw, code):
     s = shape(**kw)

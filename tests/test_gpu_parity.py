@@ -7,6 +7,8 @@ are compared element by element over the whole tensor; the large layers
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -82,13 +84,27 @@ def check_routing(s, f, dv, tag):
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_small_layer_full_parity(name):
-    s = CASES[name]
-    inp = make_inputs(s, seed=7 + len(name))
+    layer_parity(CASES[name], name, seed=7 + len(name))
+
+
+# The pages' merge ablations on two of the shapes above (one with the shared
+# head on group 1, one spanning several attention tiles).
+VARIANT_CASES = [(v, base) for v in ("weighted_concat", "hard_concat", "no_shared")
+                 for base in ("ragged_bias_k2", "multi_tile")]
+
+
+@pytest.mark.parametrize("variant,base", VARIANT_CASES, ids=[f"{v}-{b}" for v, b in VARIANT_CASES])
+def test_variant_full_parity(variant, base):
+    layer_parity(dataclasses.replace(CASES[base], variant=variant), f"{variant}/{base}", seed=31 + len(base))
+
+
+def layer_parity(s, name, seed):
+    inp = make_inputs(s, seed=seed)
     f = H.f64_inputs(inp)
     dv = H.to_device(inp)
     print(f"[case {name}] {s}", flush=True)
     idx, w, (lref, sref, wref), near, bad = check_routing(s, f, dv, name)
-    ref = go.gqe_forward(f, s.G, s.M, s.k, s.d, s.B, s.T, shared_kv_group=s.shared_kv_group)
+    ref = go.gqe_forward(f, s.G, s.M, s.k, s.d, s.B, s.T, shared_kv_group=s.shared_kv_group, variant=s.variant)
 
     # Full path: idx_out must equal gqe_route's, out must match on every row
     # whose routing agrees with the oracle.

@@ -39,14 +39,15 @@ class Shape:
     dtype: str = "bf16"          # "bf16" or "f32": storage type of x, weights, out
     router_bias: bool = False
     shared_kv_group: int = 0
+    variant: str = "full"        # merge: "full" or an ablation ("weighted_concat", "hard_concat", "no_shared")
 
     @property
     def N(self) -> int:
         return self.B * self.T
 
     @property
-    def slots(self) -> int:      # hard slots + weighted slot + shared slot
-        return self.G * self.k + 2
+    def slots(self) -> int:      # hard slots + weighted slot + shared slot (one fewer for the ablations)
+        return self.G * self.k + (2 if self.variant == "full" else 1)
 
     @property
     def Hq(self) -> int:         # dense GQA query heads over the same expert pool
