@@ -194,6 +194,70 @@ gqe_status gqa_attn_fwd_timed(int64_t B, int64_t T, int64_t D, int32_t Hq, int32
                               const void* Wv, const void* Wo, void* out,
                               void* ws, size_t ws_bytes, void* stream, void* const* events);
 
+/* ---------------------------------------------------------------------------
+ * Training: a forward that keeps its state for the backward, and the backward.
+ * Gradients of L = <dout, out> + L_aux through the full layer (GQE_FULL, bf16
+ * inputs; other variants and fp32 layers return GQE_ERR_UNSUPPORTED).
+ * [GQE-x] "Architecture and routing" (the hard concatenation carries no
+ * routing gradient; the renormalised weighted slot is the router's path) and
+ * "Training and loss" (a load-balancing auxiliary loss); [GQE-n] part 5 (the
+ * router learns through the weighted sum; balancing keeps experts in use).
+ * The picks themselves are piecewise constant: no gradient flows through idx.
+ * L_aux = aux_coef * (1/G) * sum_g M * sum_m f[g,m] * P[g,m], f[g,m] the share
+ * of group g's B*T*k picks that chose expert m, P[g,m] the mean over tokens of
+ * the router probability (the pages name such a loss but give no formula;
+ * this is the common fraction-times-probability form, per group).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace the pair gqe_attn_fwd_train / gqe_attn_bwd needs
+ * (0 if the shape is invalid or unsupported for training). */
+size_t gqe_train_workspace_bytes(const gqe_shape* s);
+
+/* gqe_attn_fwd with the same arguments and results, which also leaves in ws
+ * what gqe_attn_bwd reads (routing, projections, merged slots, and each
+ * attention row's log-sum-exp). ws_bytes >= gqe_train_workspace_bytes(s). */
+gqe_status gqe_attn_fwd_train(const gqe_shape* s, const void* x, const void* Wr, const float* br,
+                              const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh,
+                              const void* Wo, void* out, int32_t* idx_out, float* w_out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the layer. ws must be the workspace of the last
+ * gqe_attn_fwd_train with the same shape and inputs on this stream, unchanged
+ * since (the call overwrites its backward part).
+ *   x, Wr, Wq, Wk, Wv, Wq_sh, Wo   the forward's inputs (bf16, layouts as in
+ *                                  gqe_attn_fwd_routed; br is not needed)
+ *   dout     [B*T, D] bf16         gradient of the loss with respect to out
+ *   aux_coef                       weight of the load-balancing loss (finite)
+ *   dx       [B*T, D] fp32         out: gradient of x
+ *   dWr      [G*M, D] fp32         out: router weight
+ *   dbr      [G*M] fp32 or NULL    out: router offsets (NULL to skip)
+ *   dWq      [G*M*d_h, D] fp32     out: expert queries (zero rows for experts
+ *                                  no token picked)
+ *   dWk, dWv [G*d_h, D] fp32       out
+ *   dWq_sh   [d_h, D] fp32         out
+ *   dWo      [D, (G*k+2)*d_h] fp32 out
+ *   aux_loss [1] fp32 or NULL      out: the value of L_aux
+ * Gradient outputs are written, not accumulated. Deterministic: the same
+ * inputs on the same device give bit-identical results (no atomics).
+ * Errors as for gqe_attn_fwd; GQE_ERR_SHAPE also for a non-finite aux_coef. */
+gqe_status gqe_attn_bwd(const gqe_shape* s, const void* x, const void* Wr, const void* Wq,
+                        const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo,
+                        const void* dout, float aux_coef, float* dx, float* dWr, float* dbr,
+                        float* dWq, float* dWk, float* dWv, float* dWq_sh, float* dWo,
+                        float* aux_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* Instrumented gqe_attn_bwd (events as for gqe_attn_fwd_timed, GQE_BWD_N_STAGES+1
+ * entries). Stages: 0 operand layouts (transposes), 1 slot gradients dC = dout Wo
+ * and dWo, 2 attention-row preparation and router backward, 3 attention dK/dV,
+ * 4 attention dQ, 5 dx, 6 weight gradients of Wq, Wk, Wv, Wq_sh, Wr. */
+#define GQE_BWD_N_STAGES 7
+gqe_status gqe_attn_bwd_timed(const gqe_shape* s, const void* x, const void* Wr, const void* Wq,
+                              const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo,
+                              const void* dout, float aux_coef, float* dx, float* dWr, float* dbr,
+                              float* dWq, float* dWk, float* dWv, float* dWq_sh, float* dWo,
+                              float* aux_loss, void* ws, size_t ws_bytes, void* stream,
+                              void* const* events);
+
 /* A static, NUL-terminated description of a status code. */
 const char* gqe_status_str(gqe_status st);
 

@@ -11,6 +11,9 @@ Entry points (same names as the C ABI in include/gqe.h):
     gqe_attn_fwd(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out=None, w_out=None, ws=None)
     gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype)
     gqa_attn_fwd(B, T, D, Hq, G, d_h, dtype, x, Wq, Wk, Wv, Wo, out, ws=None)
+    gqe_train_workspace_bytes(shape)
+    gqe_attn_fwd_train(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, ws, idx_out=None, w_out=None)
+    gqe_attn_bwd(shape, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, grads, ws, dbr=None, aux_loss=None)
     gqe_status_str(code)
 """
 from __future__ import annotations
@@ -30,6 +33,11 @@ GQE_N_STAGES, GQA_N_STAGES = 8, 3
 GQE_STAGE_NAMES = ("proj_kv_qsh_router", "route", "scan", "scatter", "grouped_q", "attention",
                    "weighted_slot", "out_proj")
 GQA_STAGE_NAMES = ("proj_qkv", "attention", "out_proj")
+GQE_BWD_N_STAGES = 7
+GQE_BWD_STAGE_NAMES = ("layouts", "slot_grads_dWo", "prep_router", "attn_dkdv", "attn_dq", "dx",
+                       "dW")
+# Gradient outputs of gqe_attn_bwd, in argument order (fp32, shaped like the weights).
+BWD_GRADS = ("dx", "dWr", "dWq", "dWk", "dWv", "dWq_sh", "dWo")
 
 STATUS = {
     0: "GQE_OK", -1: "GQE_ERR_NULL", -2: "GQE_ERR_SHAPE", -3: "GQE_ERR_UNSUPPORTED",
@@ -84,6 +92,15 @@ def load() -> ctypes.CDLL:
     lib.gqe_attn_fwd_timed.restype = ctypes.c_int
     lib.gqa_attn_fwd_timed.argtypes = [I64, I64, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, S, P, P]
     lib.gqa_attn_fwd_timed.restype = ctypes.c_int
+    lib.gqe_train_workspace_bytes.argtypes = [SH]
+    lib.gqe_train_workspace_bytes.restype = S
+    lib.gqe_attn_fwd_train.argtypes = [SH, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gqe_attn_fwd_train.restype = ctypes.c_int
+    bwd = [SH, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gqe_attn_bwd.argtypes = bwd
+    lib.gqe_attn_bwd.restype = ctypes.c_int
+    lib.gqe_attn_bwd_timed.argtypes = bwd + [P]
+    lib.gqe_attn_bwd_timed.restype = ctypes.c_int
     lib.gqe_status_str.argtypes = [ctypes.c_int]
     lib.gqe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -205,3 +222,31 @@ def gqa_attn_fwd_timed(B, T, D, Hq, G, d_h, dtype, x, Wq, Wk, Wv, Wo, out, event
         ws = _workspace(gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype), x)
     _check(lib.gqa_attn_fwd_timed(B, T, D, Hq, G, d_h, dtype, _ptr(x), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
                                   _ptr(out), _ptr(ws), ws.numel(), _stream(stream), events))
+
+
+def gqe_train_workspace_bytes(shape: GqeShape) -> int:
+    """Workspace of the training pair gqe_attn_fwd_train / gqe_attn_bwd (0: unsupported shape)."""
+    return int(load().gqe_train_workspace_bytes(ctypes.byref(shape)))
+
+
+def gqe_attn_fwd_train(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, ws, idx_out=None, w_out=None, stream=None):
+    """The forward of gqe_attn_fwd that also leaves in ws what gqe_attn_bwd reads."""
+    _check(load().gqe_attn_fwd_train(ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(br), _ptr(Wq), _ptr(Wk),
+                                     _ptr(Wv), _ptr(Wq_sh), _ptr(Wo), _ptr(out), _ptr(idx_out), _ptr(w_out),
+                                     _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gqe_attn_bwd(shape, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, grads, ws, dbr=None, aux_loss=None,
+                 stream=None, events=None):
+    """Gradients of <dout, out> + aux loss, after gqe_attn_fwd_train on the same
+    ws. grads: dict of fp32 device tensors named as BWD_GRADS; events: optional
+    ctypes array (GQE_BWD_N_STAGES + 1 entries) recorded around the stages."""
+    lib = load()
+    args = [ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wq_sh), _ptr(Wo),
+            _ptr(dout), ctypes.c_float(aux_coef), _ptr(grads["dx"]), _ptr(grads["dWr"]), _ptr(dbr),
+            _ptr(grads["dWq"]), _ptr(grads["dWk"]), _ptr(grads["dWv"]), _ptr(grads["dWq_sh"]),
+            _ptr(grads["dWo"]), _ptr(aux_loss), _ptr(ws), ws.numel(), _stream(stream)]
+    if events is None:
+        _check(lib.gqe_attn_bwd(*args))
+    else:
+        _check(lib.gqe_attn_bwd_timed(*args, events))

@@ -49,7 +49,20 @@ struct AttnArgs {
     int32_t n_o;         // row tiles per sequence of a regular group (R rows per token)
     int32_t n_x;         // row tiles per sequence of group kv1 when it carries the extra head
     int32_t o1_col;
+    // Optional (training forward): log2-domain log-sum-exp of every row,
+    // lse[row_base(g, b) + row] with row = t*Rg + r, where a sequence of a
+    // regular group spans lse_Lr rows and one of group kv1 (extra head) lse_Lx.
+    float* lse;
+    int64_t lse_Lr, lse_Lx;
 };
+
+// First LSE row of group g, sequence b: groups in order, each sequence of a
+// regular group lse_Lr rows, of the extra head's group lse_Lx rows.
+__device__ __forceinline__ int64_t attn_lse_base(const AttnArgs& a, int g, int b) {
+    const bool xg = a.Q1 != nullptr && g == a.kv1;
+    const int64_t before = (int64_t)a.Bt * ((int64_t)g * a.lse_Lr + ((a.Q1 != nullptr && g > a.kv1) ? a.lse_Lx - a.lse_Lr : 0));
+    return before + (int64_t)b * (xg ? a.lse_Lx : a.lse_Lr);
+}
 
 // Tile shape: queries per wave, waves per workgroup, waves per SIMD the
 // register budget is sized for, keys per tile.
@@ -451,12 +464,15 @@ void attn_fwd_kernel(AttnArgs a) {
     // Normalise and store. The denominator sits in row 0 of lsum (lanes of
     // lane group 0, element 0); lane holds query l16 of block qb, columns
     // cb*16 + 4*q4 + v.
+    const int64_t lse0 = a.lse != nullptr ? attn_lse_base(a, g, b) : 0;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = __shfl(lsum[qb][0], l16);
         const float inv = 1.f / l;
         const int rho = row0 + qb * 16 + l16;
         if (rho >= n_rows) continue;
+        // p = exp2(s - m) / l, so log2 of the normaliser is m + log2(l).
+        if (a.lse != nullptr && q4 == 0) a.lse[lse0 + rho] = __builtin_amdgcn_logf(l) - minit[qb][0];
         T* orow = o_row(tq[qb], rho % Rg);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {

@@ -1,0 +1,474 @@
+// Causal flash-attention backward for the GQE layer: every picked expert and
+// the shared head attend over their group's K/V ("Grouped Query Experts"
+// explainer, technical summary, "Architecture and routing"; FrontiersMind GQE
+// article, part 4), so the gradients of a group's K and V sum over all of
+// the group's query rows, routed and shared.
+//
+// With scores s = q.k / sqrt(d), P the row softmax, dO the output gradient
+// and delta = rowsum(dO * O):
+//   dP = dO V^T,  dS = P * (dP - delta),
+//   dV = P^T dO,  dK = dS^T q / sqrt(d),  dQ = dS K / sqrt(d).
+// Queries are stored pre-scaled, Qs = q log2(e) / sqrt(d), and the forward
+// saved lse = log2 of each row's normaliser, so P = exp2(Qs.k - lse) with
+// no per-score scaling, and dK = ln(2) * dS^T Qs.
+//
+// Two kernels, no atomics (deterministic):
+//   * attn_bwd_dkdv_kernel: one workgroup per (group, sequence, 128 keys);
+//     each wave keeps 32 keys' K and V as resident MFMA operands and
+//     accumulates their dK^T, dV^T over every query row at or after the
+//     keys, 64 rows per step staged in LDS (Q, dO row-major for the score
+//     products, Q^T and dO^T for the accumulations, lse and delta);
+//   * attn_bwd_dq_kernel: one workgroup per (group, sequence, 256 rows) as
+//     in the forward; each wave keeps its 32 rows' Q and dO resident and
+//     walks the key tiles up to its last token, staging K, V (row-major) and
+//     K^T in LDS, accumulating dQ^T = K^T dS^T.
+// Score blocks are oriented so that the probabilities / score gradients a
+// lane holds after the exponent are exactly the fragment the next product
+// wants (no shuffles): the rows of a 16-row block are permuted so that the 8
+// values a lane holds over a block pair are 8 consecutive rows (keys or
+// queries), and the matching operand is one 16-byte LDS read.
+#pragma once
+
+#include "attention.hpp"
+#include "backward.hpp"
+
+namespace gqe {
+
+struct AttnBwdArgs {
+    const bf16* Q;        // [rows][d], row space of RowSpace (pre-scaled queries)
+    const bf16* Qt;       // per sequence [d][L]
+    const bf16* dO;       // [rows][d]
+    const bf16* dOt;      // per sequence [d][L]
+    const float* lse;     // [rows], +inf on padding rows
+    const float* dlt;     // [rows]
+    const bf16* K;        // [G][Bt][Tpad][d]
+    const bf16* V;        // [G][Bt][Tpad][d], zero beyond T
+    const bf16* Kt;       // [G][d][Bt*Tpad], zero beyond T
+    bf16* dY;             // [N][ldy] gradient matrix
+    const int32_t* idx;   // [N][G*k]
+    int64_t ldy;
+    int64_t Tpad;
+    RowSpace rs;
+    int32_t G, M, k;
+    int32_t colK, colV, colQsh;
+    int32_t n_tiles;      // grid levels (key tiles / row tiles per sequence, the largest class)
+};
+
+constexpr int kBwdKW = 32;         // keys per wave (dK/dV kernel)
+constexpr int kBwdNW = 4;          // waves per dK/dV workgroup
+constexpr int kBwdBK = kBwdKW * kBwdNW;
+constexpr int kBwdQB = 64;         // query rows per step (dK/dV kernel)
+constexpr int kBwdDqNW = 8;        // waves per dQ workgroup (32 rows each)
+constexpr int kBwdDqBQ = kBwdDqNW * 32;
+constexpr int kBwdBKV = 128;       // keys per tile (dQ kernel)
+
+// Row of a 64-row step held by row i of 16-row block qb (the same order as
+// key_of_row): the 8 entries a lane holds over blocks 2j, 2j+1 are rows
+// 32j + 8*(lane/16) .. +7.
+__device__ __forceinline__ int qrow_of(int qb, int i) { return key_of_row(qb, i); }
+
+template <int D>
+__global__ __launch_bounds__(kBwdNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+    constexpr int NT = kBwdNW * 64;
+    constexpr int DK = D / 32;                 // contraction steps over d
+    constexpr int CB = D / 16;                 // 16-row blocks of dK^T / dV^T
+    constexpr int QCH = D / 8;                 // 16-byte chunks per Q / dO row
+    constexpr int TCH = kBwdQB / 8;            // 16-byte chunks per Q^T / dO^T row (64 rows)
+    constexpr int R_BYTES = kBwdQB * D * 2;    // one row-major tile
+    constexpr int T_BYTES = D * kBwdQB * 2;    // one transposed tile
+    constexpr int AUX = 1024;                  // lse (256 B), delta (256 B), padding
+    constexpr int STAGE = 2 * R_BYTES + 2 * T_BYTES + AUX;
+    constexpr int R_PER_T = kBwdQB * QCH / NT;
+    constexpr int T_PER_T = D * TCH / NT;
+    static_assert(kBwdQB * QCH % NT == 0 && D * TCH % NT == 0, "tiles split evenly over the threads");
+    __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
+    __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    // Workgroup -> (level = key tile, unit = group x sequence); units of one
+    // level run back to back, longest (earliest keys) first.
+    const int units = a.G * a.rs.Bt;
+    const int kt = blockIdx.x / units, unit = blockIdx.x % units;
+    const int g = unit / a.rs.Bt, b = unit % a.rs.Bt;
+    const int64_t T_ = a.rs.T;
+    const int k0 = kt * kBwdBK;
+    if (k0 >= T_) return;
+    const int Rg = rs_R(a.rs, g);
+    const int64_t L = rs_L(a.rs, g), Lreal = T_ * Rg;
+    const int64_t base = rs_base(a.rs, g, b);
+    const int kw = k0 + wave * kBwdKW;                    // first key of this wave
+
+    // Resident B operands: K^T and V^T fragments of the wave's keys
+    // (column key = kw + 16kb + l16, contraction chunk 8*q4 of step dk).
+    const bf16* Kg = a.K + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
+    const bf16* Vg = a.V + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
+    Frag<bf16> kf[2][DK], vf[2][DK];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            const int64_t off = (int64_t)(kw + 16 * kb + l16) * D + dk * 32 + 8 * q4;
+            kf[kb][dk] = ld_frag<bf16>(Kg + off);
+            vf[kb][dk] = ld_frag<bf16>(Vg + off);
+        }
+    f32x4 dkt[CB][2], dvt[CB][2];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dkt[cb][kb] = dvt[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Steps: 64-row blocks from the first row whose token reaches k0.
+    const int64_t jb0 = ((int64_t)k0 * Rg) / kBwdQB;
+    const int64_t jb1 = (Lreal + kBwdQB - 1) / kBwdQB;
+    const int n_steps = (int)(jb1 - jb0);
+
+    // Direct global->LDS staging; per-thread offsets relative to the step's first row.
+    int roff[R_PER_T];
+    int toff[T_PER_T];
+#pragma unroll
+    for (int i = 0; i < R_PER_T; ++i) {
+        const int s = tid + NT * i, r = s / QCH, p = s % QCH;
+        roff[i] = r * D + (p ^ (((r & 3) | (((r >> 3) & 1) << 2)) & (QCH - 1))) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < T_PER_T; ++i) {
+        const int s = tid + NT * i, r = s / TCH, p = s % TCH;
+        toff[i] = (int)(r * L) + (p ^ (r & (TCH - 1))) * 8;   // r*L < 2^31: checked on the host
+    }
+    const bf16* Qb = a.Q + base * D;
+    const bf16* dOb = a.dO + base * D;
+    const bf16* Qtb = a.Qt + base * D;
+    const bf16* dOtb = a.dOt + base * D;
+    auto stage_ptr = [&](auto st) -> char* { return decltype(st)::value == 0 ? lds_a : lds_b; };
+    auto dma = [&](int j, auto st) {
+        const int64_t r0 = (jb0 + j) * kBwdQB;
+        char* S = stage_ptr(st);
+#pragma unroll
+        for (int i = 0; i < R_PER_T; ++i) {
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Qb + r0 * D + roff[i]),
+                                             (__attribute__((address_space(3))) void*)(S + (NT * i + 64 * wave) * 16), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(dOb + r0 * D + roff[i]),
+                                             (__attribute__((address_space(3))) void*)(S + R_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < T_PER_T; ++i) {
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Qtb + r0 + toff[i]),
+                                             (__attribute__((address_space(3))) void*)(S + 2 * R_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(dOtb + r0 + toff[i]),
+                                             (__attribute__((address_space(3))) void*)(S + 2 * R_BYTES + T_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
+        }
+        if (wave == 0) {   // lanes 0-15: lse, 16-31: delta, 32-63: a copy of lse into the padding
+            const float* src = (lane & 16) && lane < 32 ? a.dlt : a.lse;
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + base + r0 + 4 * (lane & 15)),
+                                             (__attribute__((address_space(3))) void*)(S + 2 * R_BYTES + 2 * T_BYTES), 16, 0, 0);
+        }
+    };
+
+    auto step = [&](int j, auto st) {
+        constexpr int SI = decltype(st)::value;
+        if (j + 1 < n_steps) dma(j + 1, StageC<SI ^ 1>{});
+        const int64_t r0 = (jb0 + j) * kBwdQB;
+        const char* S = stage_ptr(st);
+        const char* Qs = S;
+        const char* dOs = S + R_BYTES;
+        const char* Qts = S + 2 * R_BYTES;
+        const char* dOts = Qts + T_BYTES;
+        const char* aux = dOts + T_BYTES;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {          // rows 32h .. 32h+31 of the step
+            const int64_t rlo = r0 + 32 * h;
+            const int t_lo = (int)(rlo / Rg), t_hi = (int)((rlo + 31) / Rg);
+            if (kw > t_hi || rlo >= Lreal) continue;          // every key after every row's token
+            f32x4 s[2][2], dp[2][2];                           // [qb of the half][kb]
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int qb = 2 * h + qq;
+                const int chunk = 8 * (qb >> 1) + 2 * q4 + (qb & 1);   // rows 4*chunk .. +3
+                const f32x4 ls = *reinterpret_cast<const f32x4*>(aux + 16 * chunk);
+                const f32x4 dl = *reinterpret_cast<const f32x4*>(aux + 256 + 16 * chunk);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    s[qq][kb] = -ls;
+                    dp[qq][kb] = -dl;
+                }
+                const int qr = qrow_of(qb, l16);
+#pragma unroll
+                for (int dk = 0; dk < DK; ++dk) {
+                    const int c = 4 * dk + q4;
+                    const Frag<bf16> qf = ld_frag<bf16>(Qs + k_chunk_off<QCH>(qr, c));
+                    const Frag<bf16> of = ld_frag<bf16>(dOs + k_chunk_off<QCH>(qr, c));
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        s[qq][kb] = mma16(qf, kf[kb][dk], s[qq][kb]);
+                        dp[qq][kb] = mma16(of, vf[kb][dk], dp[qq][kb]);
+                    }
+                }
+            }
+            const bool mask = kw + kBwdKW - 1 > t_lo;
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = s[qq][kb][v];
+                        if (mask) {
+                            const int64_t rho = r0 + qrow_of(2 * h + qq, 4 * q4 + v);
+                            if (kw + 16 * kb + l16 > (int)(rho / Rg)) x = -INFINITY;
+                        }
+                        const float pv = __builtin_amdgcn_exp2f(x);
+                        s[qq][kb][v] = pv;
+                        dp[qq][kb][v] = pv * dp[qq][kb][v];
+                    }
+            // P and dS fragments: lane group q4 holds rows 32h + 8*q4 .. +7 of key column l16.
+            Frag<bf16> pf[2], sf[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    pf[kb].v[v] = (bf16)s[0][kb][v];
+                    pf[kb].v[4 + v] = (bf16)s[1][kb][v];
+                    sf[kb].v[v] = (bf16)dp[0][kb][v];
+                    sf[kb].v[4 + v] = (bf16)dp[1][kb][v];
+                }
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int c = cb * 16 + l16, ch = 4 * h + q4;
+                const Frag<bf16> of = ld_frag<bf16>(dOts + v_chunk_off<TCH>(c, ch));
+                const Frag<bf16> qf = ld_frag<bf16>(Qts + v_chunk_off<TCH>(c, ch));
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    dvt[cb][kb] = mma16(of, pf[kb], dvt[cb][kb]);
+                    dkt[cb][kb] = mma16(qf, sf[kb], dkt[cb][kb]);
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    if (n_steps > 0) {
+        dma(0, StageC<0>{});
+        __syncthreads();
+        for (int j = 0; j < n_steps; j += 2) {
+            step(j, StageC<0>{});
+            if (j + 1 < n_steps) step(j + 1, StageC<1>{});
+        }
+    }
+
+    // dK = ln2 * dS^T Qs, dV = P^T dO: lane holds key kw + 16kb + l16,
+    // columns 16cb + 4*q4 .. +3.
+    constexpr float kLn2 = 0.69314718055994531f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw + 16 * kb + l16;
+        if (key >= T_) continue;
+        bf16* row = a.dY + ((int64_t)b * T_ + key) * a.ldy;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int c = g * D + cb * 16 + 4 * q4;
+            bf16x4 wk, wv;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                wk[v] = (bf16)(dkt[cb][kb][v] * kLn2);
+                wv[v] = (bf16)dvt[cb][kb][v];
+            }
+            *reinterpret_cast<bf16x4*>(row + a.colK + c) = wk;
+            *reinterpret_cast<bf16x4*>(row + a.colV + c) = wv;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdDqNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(AttnBwdArgs a) {
+    constexpr int NT = kBwdDqNW * 64;
+    constexpr int BKV = kBwdBKV;
+    constexpr int DK = D / 32;
+    constexpr int CB = D / 16;
+    constexpr int KCH = D / 8;                 // chunks per K / V row
+    constexpr int VCH = BKV / 8;               // chunks per K^T row
+    constexpr int K_BYTES = BKV * D * 2;
+    constexpr int STAGE = 3 * K_BYTES;
+    constexpr int K_PER_T = BKV * KCH / NT;
+    constexpr int T_PER_T = D * VCH / NT;
+    static_assert(BKV * KCH % NT == 0 && D * VCH % NT == 0, "tiles split evenly over the threads");
+    __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
+    __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    // Workgroup -> (level, unit); level l takes row tile n_t(g) - 1 - l, so
+    // the longest tiles of every group and sequence come first.
+    const int units = a.G * a.rs.Bt;
+    const int lv = blockIdx.x / units, unit = blockIdx.x % units;
+    const int g = unit / a.rs.Bt, b = unit % a.rs.Bt;
+    const int Rg = rs_R(a.rs, g);
+    const int64_t T_ = a.rs.T;
+    const int64_t Lreal = T_ * Rg;
+    const int n_t = (int)((Lreal + kBwdDqBQ - 1) / kBwdDqBQ);
+    const int qt = n_t - 1 - lv;
+    if (qt < 0) return;
+    const int64_t base = rs_base(a.rs, g, b);
+    const int64_t row0 = (int64_t)qt * kBwdDqBQ + wave * 32;    // first row of this wave
+
+    const bf16* Qb = a.Q + base * D;
+    const bf16* dOb = a.dO + base * D;
+    Frag<bf16> qf[2][DK], of[2][DK];
+    float nls[2], ndl[2];
+    int tq[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int64_t rho = row0 + 16 * qb + l16;               // < L: padding rows are readable
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            qf[qb][dk] = ld_frag<bf16>(Qb + rho * D + dk * 32 + 8 * q4);
+            of[qb][dk] = ld_frag<bf16>(dOb + rho * D + dk * 32 + 8 * q4);
+        }
+        nls[qb] = -a.lse[base + rho];
+        ndl[qb] = -a.dlt[base + rho];
+        tq[qb] = (int)(rho / Rg);
+    }
+    const int t_first = (int)(row0 / Rg);
+    const int t_last = (int)min<int64_t>(T_ - 1, (row0 + 31) / Rg);
+    const int t_tile = (int)min<int64_t>(T_ - 1, ((int64_t)qt * kBwdDqBQ + kBwdDqBQ - 1) / Rg);
+    const int n_kv = t_tile / BKV + 1;
+
+    f32x4 dqt[CB][2];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) dqt[cb][0] = dqt[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t vrow = (int64_t)a.rs.Bt * a.Tpad;
+    const bf16* Kg = a.K + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
+    const bf16* Vg = a.V + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
+    const bf16* Ktg = a.Kt + (int64_t)g * D * vrow + (int64_t)b * a.Tpad;
+    int koff[K_PER_T];
+    int64_t toff[T_PER_T];
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+        const int s = tid + NT * i, r = s / KCH, p = s % KCH;
+        koff[i] = r * D + (p ^ (((r & 3) | (((r >> 3) & 1) << 2)) & (KCH - 1))) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < T_PER_T; ++i) {
+        const int s = tid + NT * i, r = s / VCH, p = s % VCH;
+        toff[i] = (int64_t)r * vrow + (p ^ (r & (VCH - 1))) * 8;
+    }
+    auto stage_ptr = [&](auto st) -> char* { return decltype(st)::value == 0 ? lds_a : lds_b; };
+    auto dma = [&](int j, auto st) {
+        const int64_t k0 = (int64_t)j * BKV;
+        char* S = stage_ptr(st);
+#pragma unroll
+        for (int i = 0; i < K_PER_T; ++i) {
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kg + k0 * D + koff[i]),
+                                             (__attribute__((address_space(3))) void*)(S + (NT * i + 64 * wave) * 16), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vg + k0 * D + koff[i]),
+                                             (__attribute__((address_space(3))) void*)(S + K_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < T_PER_T; ++i)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Ktg + k0 + toff[i]),
+                                             (__attribute__((address_space(3))) void*)(S + 2 * K_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
+    };
+
+    auto tile = [&](int j, auto st) {
+        constexpr int SI = decltype(st)::value;
+        if (j + 1 < n_kv) dma(j + 1, StageC<SI ^ 1>{});
+        const int k0 = j * BKV;
+        const char* Ks = stage_ptr(st);
+        const char* Vs = Ks + K_BYTES;
+        const char* Kts = Vs + K_BYTES;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {          // keys 64h .. 64h+63 of the tile
+            const int kh = k0 + 64 * h;
+            if (kh > t_last) continue;
+            f32x4 s[4][2], dp[4][2];            // [kb of the half][qb]
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                s[kb][0] = f32x4{nls[0], nls[0], nls[0], nls[0]};
+                s[kb][1] = f32x4{nls[1], nls[1], nls[1], nls[1]};
+                dp[kb][0] = f32x4{ndl[0], ndl[0], ndl[0], ndl[0]};
+                dp[kb][1] = f32x4{ndl[1], ndl[1], ndl[1], ndl[1]};
+            }
+#pragma unroll
+            for (int dk = 0; dk < DK; ++dk)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int kr = key_of_row(4 * h + kb, l16), c = 4 * dk + q4;
+                    const Frag<bf16> kfr = ld_frag<bf16>(Ks + k_chunk_off<KCH>(kr, c));
+                    const Frag<bf16> vfr = ld_frag<bf16>(Vs + k_chunk_off<KCH>(kr, c));
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        s[kb][qb] = mma16(kfr, qf[qb][dk], s[kb][qb]);
+                        dp[kb][qb] = mma16(vfr, of[qb][dk], dp[kb][qb]);
+                    }
+                }
+            const bool mask = kh + 63 > t_first;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = s[kb][qb][v];
+                        if (mask && k0 + key_of_row(4 * h + kb, 4 * q4 + v) > tq[qb]) x = -INFINITY;
+                        s[kb][qb][v] = __builtin_amdgcn_exp2f(x) * dp[kb][qb][v];
+                    }
+            // dS^T fragments: lane q4 holds keys 32kc + 8*q4 .. +7 (kc = 2h + kk) of query l16.
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                Frag<bf16> sf[2];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        sf[qb].v[v] = (bf16)s[2 * kk][qb][v];
+                        sf[qb].v[4 + v] = (bf16)s[2 * kk + 1][qb][v];
+                    }
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const Frag<bf16> ktf = ld_frag<bf16>(Kts + v_chunk_off<VCH>(cb * 16 + l16, 4 * (2 * h + kk) + q4));
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) dqt[cb][qb] = mma16(ktf, sf[qb], dqt[cb][qb]);
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    dma(0, StageC<0>{});
+    __syncthreads();
+    for (int j = 0; j < n_kv; j += 2) {
+        tile(j, StageC<0>{});
+        if (j + 1 < n_kv) tile(j + 1, StageC<1>{});
+    }
+
+    // dq = dS K / sqrt(d): lane holds row row0 + 16qb + l16, columns 16cb + 4*q4 .. +3.
+    const float sc = 1.f / sqrtf((float)D);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int64_t rho = row0 + 16 * qb + l16;
+        if (rho >= Lreal) continue;
+        const int t = tq[qb], r = (int)(rho - (int64_t)t * Rg);
+        const int64_t n = (int64_t)b * T_ + t;
+        int col = a.colQsh;
+        if (r < a.k) {
+            const int m = a.idx[n * a.G * a.k + g * a.k + r];
+            if (m < 0 || m >= a.M) continue;   // not a pick the forward can make: nothing to store
+            col = (g * a.M + m) * D;
+        }
+        bf16* row = a.dY + n * a.ldy + col;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            bf16x4 w4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) w4[v] = (bf16)(dqt[cb][qb][v] * sc);
+            *reinterpret_cast<bf16x4*>(row + cb * 16 + 4 * q4) = w4;
+        }
+    }
+}
+
+}  // namespace gqe

@@ -304,7 +304,14 @@ struct ProjArgs {
     int32_t d;           // head width (OUT_HEADS*)
     int32_t n_segs;
     int32_t n_tiles_n;
+    // Split-K (weight gradients, whose contraction runs over every token):
+    // n_split > 1 splits K into runs of k_split elements (a multiple of the
+    // K step); split s reads A and W from element s*k_split on and writes its
+    // partial product at out + s*split_stride (OUT_ROWS_F32 only, no bias).
+    int32_t n_split;
+    int32_t k_split;
     int32_t pad_;
+    int64_t split_stride;
     ProjSeg seg[4];
 };
 
@@ -312,25 +319,32 @@ template <typename T, class Cfg>
 __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* lds1, int64_t hw) {
     const int tid = threadIdx.x;
     const int64_t n_m = (a.M_rows + Cfg::BM - 1) / Cfg::BM;
-    const int64_t L = xcd_logical_id(hw, n_m * a.n_tiles_n);
+    const int64_t tiles = n_m * a.n_tiles_n;
+    const int ns = a.n_split > 1 ? a.n_split : 1;
+    const int64_t L0 = xcd_logical_id(hw, tiles * ns);
+    const int ksp = (int)(L0 / tiles);
+    const int64_t L = L0 - (int64_t)ksp * tiles;
     const int64_t m0 = (L / a.n_tiles_n) * Cfg::BM;
     const int n0 = (int)(L % a.n_tiles_n) * Cfg::BN;
+    const int koff = ns > 1 ? ksp * a.k_split : 0;
+    const int Keff = ns > 1 ? min(a.k_split, a.K - koff) : a.K;
+    const int64_t so = ns > 1 ? ksp * a.split_stride : 0;
 
     const T* a_row[Cfg::A_PER_THREAD];
     const T* b_row[Cfg::B_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
         const int64_t r = m0 + tid / 8 + Cfg::RPP * i;
-        a_row[i] = (const T*)a.A + (r < a.M_rows ? r : m0) * a.lda + (tid & 7) * Cfg::VEC;
+        a_row[i] = (const T*)a.A + (r < a.M_rows ? r : m0) * a.lda + koff + (tid & 7) * Cfg::VEC;
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_THREAD; ++i) {
         const int vc = n0 + tid / 8 + Cfg::RPP * i;
-        b_row[i] = (const T*)a.seg[0].W + (tid & 7) * Cfg::VEC;   // columns past every block
+        b_row[i] = (const T*)a.seg[0].W + koff + (tid & 7) * Cfg::VEC;   // columns past every block
         for (int s = 0; s < a.n_segs; ++s) {
             const int c = vc - a.seg[s].col_begin;
             if (c >= 0 && c < a.seg[s].n_cols)
-                b_row[i] = (const T*)a.seg[s].W + (int64_t)c * a.K + (tid & 7) * Cfg::VEC;
+                b_row[i] = (const T*)a.seg[s].W + (int64_t)c * a.K + koff + (tid & 7) * Cfg::VEC;
         }
     }
     static_assert(kProjClassAlign % Cfg::BN == 0, "a column tile holds one output class");
@@ -366,7 +380,7 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* l
 
     if (trans) {
         // Transposed heads: a lane holds tokens r .. r+3 of column c.
-        gemm_kloop<T, Cfg, false>(lds0, lds1, a_row, b_row, a.K, acc);
+        gemm_kloop<T, Cfg, false>(lds0, lds1, a_row, b_row, Keff, acc);
         const int64_t ldo = (int64_t)a.Bt * a.Tpad;
         if (fast) {
             const ProjSeg& sg = a.seg[full_seg];
@@ -413,7 +427,7 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* l
     }
 
     // Row-major outputs: a lane holds columns c .. c+3 of row r.
-    gemm_kloop<T, Cfg, true>(lds0, lds1, a_row, b_row, a.K, acc);
+    gemm_kloop<T, Cfg, true>(lds0, lds1, a_row, b_row, Keff, acc);
     if (fast) {
         const ProjSeg& sg = a.seg[full_seg];
         const int c0 = n0 - sg.col_begin + wn * Cfg::FN * 16 + 4 * (lane >> 4);
@@ -455,7 +469,7 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* l
                 const f32x4 v = acc[i][j] * sg.scale;
                 const bool full = c + 4 <= sg.n_cols;
                 if (sg.mode == OUT_ROWS_F32) {
-                    float* o = (float*)sg.out + row * sg.ld_out + c;
+                    float* o = (float*)sg.out + so + row * sg.ld_out + c;
                     float w4[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) w4[q] = v[q] + ((sg.bias && c + q < sg.n_cols) ? sg.bias[c + q] : 0.f);
@@ -495,7 +509,7 @@ __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     __shared__ __attribute__((aligned(16))) char lds_b[GQE_GEMM_DMA ? Cfg::STAGE_BYTES : 16];
     char* lds1 = GQE_GEMM_DMA ? lds_b : lds + Cfg::STAGE_BYTES;
-    const int64_t n = ((a.M_rows + Cfg::BM - 1) / Cfg::BM) * a.n_tiles_n;
+    const int64_t n = ((a.M_rows + Cfg::BM - 1) / Cfg::BM) * a.n_tiles_n * (a.n_split > 1 ? a.n_split : 1);
     for (int64_t hw = blockIdx.x; hw < n; hw += gridDim.x) proj_tile<T, Cfg>(a, lds, lds1, hw);
 }
 

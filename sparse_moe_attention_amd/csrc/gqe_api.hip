@@ -22,6 +22,8 @@
 
 #include "../../include/gqe.h"
 #include "attention.hpp"
+#include "attention_bwd.hpp"
+#include "backward.hpp"
 #include "gemm.hpp"
 #include "route.hpp"
 
@@ -133,7 +135,7 @@ void launch_proj(ProjArgs& a, int total_cols, hipStream_t st) {
     const int64_t n_m = (a.M_rows + Cfg::BM - 1) / Cfg::BM;
     // Eight resident waves per CU (two per SIMD: the register budget), in
     // whole XCD rounds.
-    const int64_t tiles = n_m * a.n_tiles_n;
+    const int64_t tiles = n_m * a.n_tiles_n * (a.n_split > 1 ? a.n_split : 1);
     const int per_cu = 8 / (Cfg::WM * Cfg::WN);
     const int64_t grid = std::min<int64_t>(tiles, per_cu * (int64_t)align_up((size_t)device_cus(), 8));
     hipLaunchKernelGGL((proj_gemm_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NTH), 0, st, a);
@@ -250,7 +252,8 @@ struct Marks {
 gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* x, const void* Wq,
                            const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo,
                            const int32_t* idx, const float* w, void* out, void* C, hipStream_t st,
-                           bool project_kv, const Marks& mk) {
+                           bool project_kv, const Marks& mk, float* lse = nullptr, int64_t lse_Lr = 0,
+                           int64_t lse_Lx = 0) {
     if (project_kv) {
         SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
         sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
@@ -281,6 +284,9 @@ gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* 
     a.R = d.k;                 // routed head j = g*k + r: hard slot j of C
     a.kv1 = d.s0;
     a.o1_col = (d.GK + (d.weighted_slot() ? 1 : 0)) * d.d;   // the shared slot is the last one
+    a.lse = lse;
+    a.lse_Lr = lse_Lr;
+    a.lse_Lx = lse_Lx;
     mk.at(5);
     run_attention(d, a, st);
     mk.at(6);
@@ -291,6 +297,345 @@ gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* 
     run_proj(d, so, st);
     mk.at(8);
     return last_hip();
+}
+
+// ---------------------------------------------------------------------------
+// Training: the forward that keeps what the backward needs, and the backward.
+// ---------------------------------------------------------------------------
+// The backward covers the full layer in bf16 (the other merge variants and
+// fp32 layers are forward-only).
+gqe_status check_train(const Dims& d) {
+    if (d.f32 || d.variant != GQE_FULL) return GQE_ERR_UNSUPPORTED;
+    return GQE_OK;
+}
+
+// The backward's gradient matrix dY [N, ccat_pad] (and its transpose): the
+// gradients of everything x is projected to, side by side, so that
+// dx = dY W_cat and dW_cat = dY^T x are one GEMM each:
+//   [dQ of every expert (zero where not picked) | dK | dV | dQ_shared | dlogits | 0].
+struct TrainWs {
+    RowSpace rs;
+    int64_t rows, Npad, ccat, ccat_pad, col_k, col_v, col_qsh, col_lg;
+    int n_cs, ns_wo, ks_wo, ns_w, ks_w;
+    // Forward state (lse) and backward buffers, after the forward's own layout.
+    size_t lse, dlt, Qc, Qt, dOc, dOt, dw, dz, p, cs, dC, WoT, WcT, xT, doT, CT, Kt, V, dY, dYt, part, total;
+};
+
+constexpr int kRowPad = kBwdDqBQ;    // row-space runs pad to whole dQ row tiles
+constexpr int kColsumRows = 1024;
+
+// Splits of a weight-gradient GEMM over its token contraction: about 1024
+// workgroups (two rounds of MI355X's 256 CUs at two per CU), runs of at
+// least 512 tokens. A function of the shape alone, so the workspace size and
+// the summation order do not depend on the device.
+void pick_splits(int64_t tiles, int64_t Kfull, int* ns, int* ks) {
+    const int64_t want = (1024 + tiles - 1) / tiles;
+    const int64_t cap = std::max<int64_t>(1, Kfull / 512);
+    int64_t n = std::min(std::max<int64_t>(want, 1), cap);
+    int64_t k = (int64_t)align_up((size_t)((Kfull + n - 1) / n), 64);
+    n = (Kfull + k - 1) / k;
+    *ns = (int)n;
+    *ks = (int)k;
+}
+
+TrainWs train_layout(const Dims& d) {
+    TrainWs L;
+    L.rs.T = d.T;
+    L.rs.Bt = (int32_t)d.B;
+    L.rs.R = d.k;
+    L.rs.s0 = d.s0;
+    L.rs.Lr = (int64_t)align_up((size_t)(d.T * d.k), kRowPad);
+    L.rs.Lx = (int64_t)align_up((size_t)(d.T * (d.k + 1)), kRowPad);
+    L.rows = d.B * ((int64_t)d.G * L.rs.Lr + (L.rs.Lx - L.rs.Lr));
+    L.Npad = (int64_t)align_up((size_t)d.N, 64);
+    L.col_k = (int64_t)d.E * d.d;
+    L.col_v = L.col_k + (int64_t)d.G * d.d;
+    L.col_qsh = L.col_v + (int64_t)d.G * d.d;
+    L.col_lg = L.col_qsh + d.d;
+    L.ccat = L.col_lg + d.E;
+    L.ccat_pad = (int64_t)align_up((size_t)L.ccat, 64);
+    L.n_cs = (int)((d.N + kColsumRows - 1) / kColsumRows);
+    const int64_t SD = (int64_t)d.slots * d.d;
+    const int64_t t_wo = ((d.D + 127) / 128) * ((SD + 127) / 128);
+    const int64_t t_w = ((L.ccat + 127) / 128) * ((d.D + 127) / 128);
+    pick_splits(t_wo, L.Npad, &L.ns_wo, &L.ks_wo);
+    pick_splits(t_w, L.Npad, &L.ns_w, &L.ks_w);
+
+    size_t o = gqe_layout(d).total;
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+    const size_t rows = (size_t)L.rows;
+    L.lse = take(rows * 4);
+    L.dlt = take(rows * 4);
+    L.Qc = take(rows * d.d * 2);
+    L.Qt = take(rows * d.d * 2);
+    L.dOc = take(rows * d.d * 2);
+    L.dOt = take(rows * d.d * 2);
+    L.dw = take((size_t)d.N * d.GK * 4);
+    L.dz = take((size_t)d.N * d.E * 4);
+    L.p = take((size_t)d.N * d.E * 4);
+    L.cs = take((size_t)2 * L.n_cs * d.E * 4);
+    L.dC = take((size_t)d.N * SD * 2);
+    L.WoT = take((size_t)SD * d.D * 2);
+    L.WcT = take((size_t)d.D * L.ccat_pad * 2);
+    L.xT = take((size_t)d.D * L.Npad * 2);
+    L.doT = take((size_t)d.D * L.Npad * 2);
+    L.CT = take((size_t)SD * L.Npad * 2);
+    L.Kt = take((size_t)d.G * d.d * d.B * d.Tpad * 2);
+    L.V = take((size_t)d.G * d.B * d.Tpad * d.d * 2);
+    L.dY = take((size_t)d.N * L.ccat_pad * 2);
+    L.dYt = take((size_t)L.ccat * L.Npad * 2);
+    L.part = take(std::max((size_t)L.ns_wo * d.D * SD, (size_t)L.ns_w * L.ccat * d.D) * 4);
+    L.total = o;
+    return L;
+}
+
+// dst[x][y] = src[y][x] (y < R, x < C), zero elsewhere in [Co x Ro]; z batches.
+void run_transpose(const bf16* src, int64_t lds, int64_t R, int64_t C, bf16* dst, int64_t ldd, int64_t Ro,
+                   int64_t Co, int z, int64_t zs, int64_t zd, hipStream_t st) {
+    if (Ro <= 0 || Co <= 0) return;
+    TrArgs t;
+    t.src = src; t.dst = dst; t.lds = lds; t.ldd = ldd;
+    t.R = R; t.C = C; t.Ro = Ro; t.Co = Co; t.zs = zs; t.zd = zd;
+    const dim3 grid((unsigned)(((Ro + 63) / 64) * ((Co + 63) / 64)), (unsigned)z);
+    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, st, t);
+}
+
+// Projection-engine GEMM out = A W^T over plain matrices (no head layouts).
+SegList gemm_base(const void* A, int64_t lda, int64_t rows, int K) {
+    SegList sl;
+    std::memset(&sl.a, 0, sizeof(sl.a));
+    sl.a.A = A;
+    sl.a.lda = lda;
+    sl.a.M_rows = rows;
+    sl.a.T = rows;
+    sl.a.Tpad = rows;
+    sl.a.Bt = 1;
+    sl.a.K = K;
+    sl.a.d = 64;
+    return sl;
+}
+
+// Weight gradient through split-K: part[s] = A_s W_s^T, then a fixed-order
+// sum scattered to the destinations (row ranges of the product).
+void run_wgrad(const void* A, int64_t lda, int64_t rows, const void* W, int64_t cols, int64_t K, int ns, int ks,
+               float* part, const RedDst* dst, int n_dst, hipStream_t st) {
+    SegList sl = gemm_base(A, lda, rows, (int)K);
+    sl.add(W, (int)cols, part, OUT_ROWS_F32, cols, nullptr);
+    sl.a.n_split = ns;
+    sl.a.k_split = ks;
+    sl.a.split_stride = rows * cols;
+    launch_proj<bf16, ProjBf16>(sl.a, sl.cols, st);
+    RedArgs r;
+    std::memset(&r, 0, sizeof(r));
+    r.part = part;
+    r.split_stride = rows * cols;
+    r.rows = rows;
+    r.cols = cols;
+    r.n_split = ns;
+    r.n_dst = n_dst;
+    for (int i = 0; i < n_dst; ++i) r.dst[i] = dst[i];
+    const int64_t items = rows * (cols / 4);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, r);
+}
+
+// Zero K rows and V^T columns of tokens in [T, Tpad): the backward's
+// transposed copies then hold zeros there.
+__global__ void kv_pad_kernel(bf16* K, bf16* Vt, int64_t T, int64_t Tpad, int Bt, int d) {
+    const int g = blockIdx.x / Bt, b = blockIdx.x % Bt;
+    const int64_t n_pad = Tpad - T;
+    bf16* kp = K + (((int64_t)g * Bt + b) * Tpad + T) * d;
+    for (int64_t i = threadIdx.x; i < n_pad * d; i += blockDim.x) kp[i] = (bf16)0.f;
+    const int64_t vrow = (int64_t)Bt * Tpad;
+    for (int64_t i = threadIdx.x; i < n_pad * d; i += blockDim.x) {
+        const int64_t c = i / n_pad, t = T + i % n_pad;
+        Vt[((int64_t)g * d + c) * vrow + (int64_t)b * Tpad + t] = (bf16)0.f;
+    }
+}
+
+gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const void* Wq, const void* Wk,
+                    const void* Wv, const void* Wq_sh, const void* Wo, const void* dout, float aux_coef, float* dx,
+                    float* dWr, float* dbr, float* dWq, float* dWk, float* dWv, float* dWq_sh, float* dWo,
+                    float* aux_loss, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+    Dims d;
+    gqe_status rc = check_shape(s, &d);
+    if (rc != GQE_OK) return rc;
+    if ((rc = check_train(d)) != GQE_OK) return rc;
+    if (!x || !Wr || !Wq || !Wk || !Wv || !Wq_sh || !Wo || !dout || !dx || !dWr || !dWq || !dWk || !dWv ||
+        !dWq_sh || !dWo || !ws)
+        return GQE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(Wr) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
+        !aligned16(Wq_sh) || !aligned16(Wo) || !aligned16(dout) || !aligned16(dx) || !aligned16(dWr) ||
+        !aligned16(dWq) || !aligned16(dWk) || !aligned16(dWv) || !aligned16(dWq_sh) || !aligned16(dWo) ||
+        !aligned16(ws) || (dbr && !aligned16(dbr)))
+        return GQE_ERR_ALIGN;
+    if (!std::isfinite(aux_coef)) return GQE_ERR_SHAPE;
+    const GqeWs F = gqe_layout(d);
+    const TrainWs L = train_layout(d);
+    if (ws_bytes < L.total) return GQE_ERR_WORKSPACE;
+    if ((int64_t)d.d * L.rs.Lx >= ((int64_t)1 << 31)) return GQE_ERR_SHAPE;   // 32-bit staging offsets
+    hipStream_t st = (hipStream_t)stream;
+    const Marks mk{events, st};
+    const int64_t SD = (int64_t)d.slots * d.d, N = d.N, D = d.D, dh = d.d;
+    const int64_t vrow = d.B * d.Tpad;
+    auto B = [&](size_t off) { return (bf16*)at(ws, off); };
+    auto F32 = [&](size_t off) { return (float*)at(ws, off); };
+
+    mk.at(0);
+    // Operand layouts: transposed weights and token-contiguous activations.
+    run_transpose((const bf16*)Wo, SD, D, SD, B(L.WoT), D, D, SD, 1, 0, 0, st);
+    bf16* wct = B(L.WcT);
+    run_transpose((const bf16*)Wq, D, (int64_t)d.E * dh, D, wct, L.ccat_pad, (int64_t)d.E * dh, D, 1, 0, 0, st);
+    run_transpose((const bf16*)Wk, D, (int64_t)d.G * dh, D, wct + L.col_k, L.ccat_pad, (int64_t)d.G * dh, D, 1, 0, 0, st);
+    run_transpose((const bf16*)Wv, D, (int64_t)d.G * dh, D, wct + L.col_v, L.ccat_pad, (int64_t)d.G * dh, D, 1, 0, 0, st);
+    run_transpose((const bf16*)Wq_sh, D, dh, D, wct + L.col_qsh, L.ccat_pad, dh, D, 1, 0, 0, st);
+    run_transpose((const bf16*)Wr, D, d.E, D, wct + L.col_lg, L.ccat_pad, L.ccat_pad - L.col_lg, D, 1, 0, 0, st);
+    run_transpose((const bf16*)x, D, N, D, B(L.xT), L.Npad, L.Npad, D, 1, 0, 0, st);
+    run_transpose((const bf16*)dout, D, N, D, B(L.doT), L.Npad, L.Npad, D, 1, 0, 0, st);
+    run_transpose(B(F.C), SD, N, SD, B(L.CT), L.Npad, L.Npad, SD, 1, 0, 0, st);
+    if (d.Tpad > d.T)
+        hipLaunchKernelGGL(kv_pad_kernel, dim3((unsigned)(d.G * d.B)), dim3(256), 0, st, B(F.K), B(F.Vt), d.T, d.Tpad,
+                           (int)d.B, d.d);
+    run_transpose(B(F.K), dh, vrow, dh, B(L.Kt), vrow, vrow, dh, d.G, vrow * dh, vrow * dh, st);
+    run_transpose(B(F.Vt), vrow, dh, vrow, B(L.V), dh, dh, vrow, d.G, vrow * dh, vrow * dh, st);
+    mk.at(1);
+
+    // Slot gradients dC = dout Wo, and dWo = dout^T C.
+    {
+        SegList sl = gemm_base(dout, D, N, (int)D);
+        sl.add(B(L.WoT), (int)SD, B(L.dC), OUT_ROWS, SD, nullptr);
+        launch_proj<bf16, ProjBf16>(sl.a, sl.cols, st);
+        const RedDst dst{dWo, 0, D};
+        run_wgrad(B(L.doT), L.Npad, D, B(L.CT), SD, L.Npad, L.ns_wo, L.ks_wo, F32(L.part), &dst, 1, st);
+    }
+    mk.at(2);
+
+    // Attention rows: dO, dw, delta and the compact copies.
+    {
+        PrepArgs pa;
+        pa.Qr = B(F.Qr); pa.Qsh = B(F.Qsh); pa.C = B(F.C); pa.dC = B(L.dC);
+        pa.w = F32(F.w);
+        pa.Qc = B(L.Qc); pa.Qt = B(L.Qt); pa.dOc = B(L.dOc); pa.dOt = B(L.dOt);
+        pa.lse = F32(L.lse); pa.dlt = F32(L.dlt); pa.dw = F32(L.dw);
+        pa.rs = L.rs;
+        pa.ldc = SD;
+        pa.G = d.G; pa.k = d.k; pa.d = d.d;
+        pa.wcol = d.GK * d.d;
+        pa.shcol = (d.GK + 1) * d.d;
+        const dim3 grid((unsigned)(L.rs.Lx / 64), (unsigned)(d.G * d.B));
+        if (d.d == 64) hipLaunchKernelGGL(prep_kernel<64>, grid, dim3(256), 0, st, pa);
+        else hipLaunchKernelGGL(prep_kernel<32>, grid, dim3(256), 0, st, pa);
+    }
+    // Router: dlogits (and the zero columns of unpicked experts), dbr, balancing loss.
+    {
+        RouterBwdArgs ra;
+        ra.logits = F32(F.logits);
+        ra.idx = (const int32_t*)at(ws, F.idx);
+        ra.w = F32(F.w);
+        ra.dw = F32(L.dw);
+        ra.offsets = (const int32_t*)at(ws, F.offsets);
+        ra.dz = F32(L.dz);
+        ra.p = F32(L.p);
+        ra.dY = B(L.dY);
+        ra.N = N;
+        ra.ldy = L.ccat_pad;
+        ra.G = d.G; ra.M = d.M; ra.k = d.k; ra.d = d.d;
+        ra.lg_col = (int)L.col_lg;
+        ra.pad_col = (int)L.ccat;
+        ra.coef = aux_coef;
+        hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, ra);
+        hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)L.n_cs), dim3(256), 0, st, (const float*)F32(L.dz),
+                           (const float*)F32(L.p), F32(L.cs), N, d.E, kColsumRows);
+        hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(256), 0, st, (const float*)F32(L.cs), L.n_cs,
+                           (const int32_t*)at(ws, F.offsets), N, d.G, d.M, d.k, aux_coef, dbr, aux_loss);
+    }
+    mk.at(3);
+
+    // Attention backward.
+    AttnBwdArgs ab;
+    ab.Q = B(L.Qc); ab.Qt = B(L.Qt); ab.dO = B(L.dOc); ab.dOt = B(L.dOt);
+    ab.lse = F32(L.lse); ab.dlt = F32(L.dlt);
+    ab.K = B(F.K); ab.V = B(L.V); ab.Kt = B(L.Kt);
+    ab.dY = B(L.dY);
+    ab.idx = (const int32_t*)at(ws, F.idx);
+    ab.ldy = L.ccat_pad;
+    ab.Tpad = d.Tpad;
+    ab.rs = L.rs;
+    ab.G = d.G; ab.M = d.M; ab.k = d.k;
+    ab.colK = (int)L.col_k; ab.colV = (int)L.col_v; ab.colQsh = (int)L.col_qsh;
+    {
+        ab.n_tiles = (int)((d.T + kBwdBK - 1) / kBwdBK);
+        const dim3 grid((unsigned)((int64_t)ab.n_tiles * d.G * d.B));
+        if (d.d == 64) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, dim3(kBwdNW * 64), 0, st, ab);
+        else hipLaunchKernelGGL(attn_bwd_dkdv_kernel<32>, grid, dim3(kBwdNW * 64), 0, st, ab);
+    }
+    mk.at(4);
+    {
+        ab.n_tiles = (int)((d.T * (d.k + 1) + kBwdDqBQ - 1) / kBwdDqBQ);
+        const dim3 grid((unsigned)((int64_t)ab.n_tiles * d.G * d.B));
+        if (d.d == 64) hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(kBwdDqNW * 64), 0, st, ab);
+        else hipLaunchKernelGGL(attn_bwd_dq_kernel<32>, grid, dim3(kBwdDqNW * 64), 0, st, ab);
+    }
+    mk.at(5);
+
+    // dx = dY W_cat, dW_cat = dY^T x.
+    run_transpose(B(L.dY), L.ccat_pad, N, L.ccat, B(L.dYt), L.Npad, L.Npad, L.ccat, 1, 0, 0, st);
+    {
+        SegList sl = gemm_base(B(L.dY), L.ccat_pad, N, (int)L.ccat_pad);
+        sl.add(B(L.WcT), (int)D, dx, OUT_ROWS_F32, D, nullptr);
+        launch_proj<bf16, ProjBf16>(sl.a, sl.cols, st);
+    }
+    mk.at(6);
+    {
+        const RedDst dst[5] = {{dWq, 0, (int64_t)d.E * dh},
+                               {dWk, L.col_k, (int64_t)d.G * dh},
+                               {dWv, L.col_v, (int64_t)d.G * dh},
+                               {dWq_sh, L.col_qsh, dh},
+                               {dWr, L.col_lg, d.E}};
+        run_wgrad(B(L.dYt), L.Npad, L.ccat, B(L.xT), D, L.Npad, L.ns_w, L.ks_w, F32(L.part), dst, 5, st);
+    }
+    mk.at(7);
+    return last_hip();
+}
+
+gqe_status fwd_impl(const gqe_shape* s, const void* x, const void* Wr, const float* br, const void* Wq,
+                    const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo, void* out, int32_t* idx_out,
+                    float* w_out, void* ws, size_t ws_bytes, void* stream, void* const* events, bool train) {
+    Dims d;
+    gqe_status rc = check_shape(s, &d);
+    if (rc != GQE_OK) return rc;
+    if (!x || !Wr || !Wq || !Wk || !Wv || !Wq_sh || !Wo || !out || !ws) return GQE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(Wr) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
+        !aligned16(Wq_sh) || !aligned16(Wo) || !aligned16(out) || !aligned16(ws) || (br && !aligned16(br)) ||
+        (idx_out && !aligned16(idx_out)) || (w_out && !aligned16(w_out)))
+        return GQE_ERR_ALIGN;
+    if (train && (rc = check_train(d)) != GQE_OK) return rc;
+    const GqeWs L = gqe_layout(d);
+    const TrainWs TL = train_layout(d);
+    if (ws_bytes < (train ? TL.total : L.total)) return GQE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    // Training keeps the routing in ws for the backward (copied out below).
+    int32_t* idx = (idx_out && !train) ? idx_out : (int32_t*)at(ws, L.idx);
+    float* w = (w_out && !train) ? w_out : (float*)at(ws, L.w);
+    float* lg = (float*)at(ws, L.logits);
+    const Marks mk{events, st};
+    mk.at(0);
+    // One pass over x: K, V^T, Q_sh and the router logits.
+    SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
+    sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
+    if (d.shared_head()) sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
+    sl.add(Wr, d.E, lg, OUT_ROWS_F32, d.E, br);
+    sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
+    run_proj(d, sl, st);
+    mk.at(1);
+    hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)lg, idx, w,
+                       (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k, (int)(d.variant != GQE_WEIGHTED_CONCAT));
+    rc = run_post_router(d, L, ws, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, at(ws, L.C), st, false, mk,
+                         train ? (float*)at(ws, TL.lse) : nullptr, TL.rs.Lr, TL.rs.Lx);
+    if (rc != GQE_OK || !train) return rc;
+    const size_t picks = (size_t)d.N * d.GK;
+    if (idx_out && hipMemcpyAsync(idx_out, idx, picks * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return GQE_ERR_HIP;
+    if (w_out && hipMemcpyAsync(w_out, w, picks * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return GQE_ERR_HIP;
+    return GQE_OK;
 }
 
 }  // namespace
@@ -353,33 +698,7 @@ gqe_status gqe_attn_fwd_timed(const gqe_shape* s, const void* x, const void* Wr,
                               const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo,
                               void* out, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream,
                               void* const* events) {
-    Dims d;
-    gqe_status rc = check_shape(s, &d);
-    if (rc != GQE_OK) return rc;
-    if (!x || !Wr || !Wq || !Wk || !Wv || !Wq_sh || !Wo || !out || !ws) return GQE_ERR_NULL;
-    if (!aligned16(x) || !aligned16(Wr) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
-        !aligned16(Wq_sh) || !aligned16(Wo) || !aligned16(out) || !aligned16(ws) || (br && !aligned16(br)) ||
-        (idx_out && !aligned16(idx_out)) || (w_out && !aligned16(w_out)))
-        return GQE_ERR_ALIGN;
-    const GqeWs L = gqe_layout(d);
-    if (ws_bytes < L.total) return GQE_ERR_WORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
-    int32_t* idx = idx_out ? idx_out : (int32_t*)at(ws, L.idx);
-    float* w = w_out ? w_out : (float*)at(ws, L.w);
-    float* lg = (float*)at(ws, L.logits);
-    const Marks mk{events, st};
-    mk.at(0);
-    // One pass over x: K, V^T, Q_sh and the router logits.
-    SegList sl = proj_base(d, x, d.D, d.N, (int)d.D);
-    sl.add(Wk, d.G * d.d, at(ws, L.K), OUT_HEADS, 0, nullptr);
-    if (d.shared_head()) sl.add(Wq_sh, d.d, at(ws, L.Qsh), OUT_ROWS, d.d, nullptr, q_scale(d));
-    sl.add(Wr, d.E, lg, OUT_ROWS_F32, d.E, br);
-    sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
-    run_proj(d, sl, st);
-    mk.at(1);
-    hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)lg, idx, w,
-                       (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k, (int)(d.variant != GQE_WEIGHTED_CONCAT));
-    return run_post_router(d, L, ws, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, at(ws, L.C), st, false, mk);
+    return fwd_impl(s, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out, w_out, ws, ws_bytes, stream, events, false);
 }
 
 gqe_status gqe_attn_fwd(const gqe_shape* s, const void* x, const void* Wr, const float* br, const void* Wq,
@@ -387,6 +706,35 @@ gqe_status gqe_attn_fwd(const gqe_shape* s, const void* x, const void* Wr, const
                         int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
     return gqe_attn_fwd_timed(s, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out, w_out, ws, ws_bytes, stream,
                               nullptr);
+}
+
+size_t gqe_train_workspace_bytes(const gqe_shape* s) {
+    Dims d;
+    if (check_shape(s, &d) != GQE_OK || check_train(d) != GQE_OK) return 0;
+    return train_layout(d).total;
+}
+
+gqe_status gqe_attn_fwd_train(const gqe_shape* s, const void* x, const void* Wr, const float* br, const void* Wq,
+                              const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo, void* out,
+                              int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
+    return fwd_impl(s, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out, w_out, ws, ws_bytes, stream, nullptr, true);
+}
+
+gqe_status gqe_attn_bwd_timed(const gqe_shape* s, const void* x, const void* Wr, const void* Wq, const void* Wk,
+                              const void* Wv, const void* Wq_sh, const void* Wo, const void* dout, float aux_coef,
+                              float* dx, float* dWr, float* dbr, float* dWq, float* dWk, float* dWv, float* dWq_sh,
+                              float* dWo, float* aux_loss, void* ws, size_t ws_bytes, void* stream,
+                              void* const* events) {
+    return bwd_impl(s, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, dx, dWr, dbr, dWq, dWk, dWv, dWq_sh, dWo,
+                    aux_loss, ws, ws_bytes, stream, events);
+}
+
+gqe_status gqe_attn_bwd(const gqe_shape* s, const void* x, const void* Wr, const void* Wq, const void* Wk,
+                        const void* Wv, const void* Wq_sh, const void* Wo, const void* dout, float aux_coef, float* dx,
+                        float* dWr, float* dbr, float* dWq, float* dWk, float* dWv, float* dWq_sh, float* dWo,
+                        float* aux_loss, void* ws, size_t ws_bytes, void* stream) {
+    return bwd_impl(s, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, dx, dWr, dbr, dWq, dWk, dWv, dWq_sh, dWo,
+                    aux_loss, ws, ws_bytes, stream, nullptr);
 }
 
 // ---------------------------------------------------------------------------

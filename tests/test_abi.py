@@ -118,3 +118,50 @@ def test_workspace_monotone_in_tokens(lib):
     # the extreme-context layer fits comfortably in one MI355X's 288 GB
     s = shape(T=1 << 20, D=1024, G=8, M=2, d_h=64)
     assert lib.gqe_workspace_bytes(ctypes.byref(s)) < 8 << 30
+
+
+def _bwd(lib, s, ws_bytes=1 << 40, coef=0.0, **over):
+    """gqe_attn_bwd with every pointer A unless overridden by name."""
+    names = ["x", "Wr", "Wq", "Wk", "Wv", "Wq_sh", "Wo", "dout", "dx", "dWr", "dbr", "dWq", "dWk", "dWv",
+             "dWq_sh", "dWo", "aux_loss", "ws"]
+    p = {n: A for n in names}
+    p.update(over)
+    return lib.gqe_attn_bwd(ctypes.byref(s), p["x"], p["Wr"], p["Wq"], p["Wk"], p["Wv"], p["Wq_sh"], p["Wo"],
+                            p["dout"], ctypes.c_float(coef), p["dx"], p["dWr"], p["dbr"], p["dWq"], p["dWk"],
+                            p["dWv"], p["dWq_sh"], p["dWo"], p["aux_loss"], p["ws"], ws_bytes, None)
+
+
+def test_train_entry_points_validate(lib):
+    s = shape()
+    need = lib.gqe_train_workspace_bytes(ctypes.byref(s))
+    assert need > lib.gqe_workspace_bytes(ctypes.byref(s)) > 0
+    fwd = lambda sh, n: lib.gqe_attn_fwd_train(ctypes.byref(sh), A, A, None, A, A, A, A, A, A, None, None, A, n,
+                                               None)
+    assert fwd(s, need - 1) == -4
+    assert _bwd(lib, s, need - 1) == -4
+    # the training pair covers the full layer in bf16 only
+    for kw in (dict(dtype=gq.GQE_F32), dict(variant=gq.GQE_HARD_CONCAT), dict(variant=gq.GQE_NO_SHARED),
+               dict(variant=gq.GQE_WEIGHTED_CONCAT)):
+        u = shape(**kw)
+        assert lib.gqe_train_workspace_bytes(ctypes.byref(u)) == 0
+        assert fwd(u, 1 << 40) == -3
+        assert _bwd(lib, u) == -3
+    assert _bwd(lib, shape(k=3)) == -2
+    assert _bwd(lib, s, dx=None) == -1
+    assert _bwd(lib, s, dout=None) == -1
+    assert _bwd(lib, s, dWo=None) == -1
+    assert _bwd(lib, s, dWq=BAD) == -5
+    assert _bwd(lib, s, dbr=BAD) == -5
+    assert _bwd(lib, s, coef=float("nan")) == -2
+    assert _bwd(lib, s, coef=float("inf")) == -2
+
+
+def test_train_workspace_sizes(lib):
+    prev = 0
+    for T in (1, 77, 256, 257, 4096, 32768):
+        s = shape(T=T, D=1024, G=8, M=2, d_h=64)
+        n = lib.gqe_train_workspace_bytes(ctypes.byref(s))
+        assert n > prev
+        prev = n
+    s = shape(T=1 << 20, D=1024, G=8, M=2, d_h=64)
+    assert lib.gqe_train_workspace_bytes(ctypes.byref(s)) < 64 << 30

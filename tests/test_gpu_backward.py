@@ -1,0 +1,150 @@
+"""GPU parity of the training pair (gqe_attn_fwd_train, gqe_attn_bwd) against
+the fp64 backward oracle, through the C ABI.
+
+Every gradient (x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo) and the balancing loss are
+compared over the whole tensor at shapes spanning several key and query
+tiles, ragged tails, k > 1, the shared head on group 1, and the degenerate
+cases (one token, one group, one expert per group, k = M). At the 32K-token
+layer the checks are properties that hold at any size: bit-identical reruns,
+exact scaling with dout, finiteness.
+
+Tolerance (bf16 arithmetic): the GPU rounds to bf16 at each hand-off of the
+chain (forward Q, K, V, O; slot gradients dC; dO; the probabilities and
+score gradients fed to the matrix cores; the gradient matrix dY), about
+seven roundings of relative size 2^-9 each, which the softmax backward can
+amplify where dP - delta cancels. Bar per gradient tensor: relative
+Frobenius error <= 3e-2 and max |error| <= 6e-2 * max |ref|.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gqe_backward as gb
+import oracle.gqe_oracle as go
+import sparse_moe_attention_amd as gq
+from tests import harness as H
+from workloads import CONFIGS, Shape, make_grad_output, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+FROB, MAXREL = 3e-2, 6e-2
+ZERO_REL = 1e-5
+AUX_REL = 1e-4
+
+CASES = {
+    "tiny": (Shape(B=1, T=64, D=64, G=2, M=2, k=1, d=32), 0.0),
+    "ragged_bias_k2": (Shape(B=3, T=200, D=128, G=3, M=3, k=2, d=32, router_bias=True, shared_kv_group=1), 0.05),
+    "multi_tile": (Shape(B=2, T=1000, D=256, G=8, M=2, k=1, d=64), 0.01),
+    "one_group": (Shape(B=1, T=300, D=192, G=1, M=4, k=2, d=64), 0.02),
+    "single_token": (Shape(B=2, T=1, D=64, G=2, M=2, k=1, d=64), 0.1),
+    "one_expert": (Shape(B=1, T=130, D=64, G=4, M=1, k=1, d=32), 0.1),
+    "all_experts": (Shape(B=2, T=150, D=128, G=2, M=3, k=3, d=64), 0.0),
+    "wide_pool": (Shape(B=1, T=260, D=128, G=4, M=16, k=4, d=32, router_bias=True), 0.03),
+    "long": (Shape(B=1, T=2048, D=512, G=4, M=2, k=1, d=64), 0.01),
+}
+
+GRADS = ("dx", "dWr", "dWq", "dWk", "dWv", "dWq_sh", "dWo")
+
+
+def run_train(s: Shape, dv: dict, dout, coef: float):
+    """Training forward then backward on the GPU; returns host fp64 results."""
+    sh = gq.shape_from(s)
+    ws = torch.empty(gq.gqe_train_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    out = torch.empty(s.N, s.D, dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(s.N, s.G, s.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(s.N, s.G, s.k, dtype=torch.float32, device="cuda")
+    gq.gqe_attn_fwd_train(sh, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"], dv["Wo"],
+                          out, ws, idx, w)
+    g = {k: torch.full_like(dv[k[1:]] if k != "dx" else dv["x"], float("nan"), dtype=torch.float32)
+         for k in GRADS}
+    dbr = torch.full((s.G * s.M,), float("nan"), dtype=torch.float32, device="cuda")
+    aux = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gqe_attn_bwd(sh, dv["x"], dv["Wr"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"], dv["Wo"], dout, coef, g, ws,
+                    dbr=dbr, aux_loss=aux)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy().astype(np.float64) for k, v in g.items()}
+    res["dbr"] = dbr.cpu().numpy().astype(np.float64)
+    res["aux"] = float(aux.item())
+    res["idx"] = idx.cpu().numpy()
+    res["out"] = H.np32(out)
+    return res
+
+
+def compare(name, key, got, ref, scale):
+    """scale: the largest reference gradient entry of the case. A gradient that
+    is zero in exact arithmetic (one key: dS = dP - delta = 0) keeps only the
+    difference of two fp32 sums of the same products on the GPU, a few fp32
+    roundings of dP: bounded by ZERO_REL * scale."""
+    assert np.isfinite(got).all(), (name, key, "non-finite")
+    nref = float(np.linalg.norm(ref))
+    frob = float(np.linalg.norm(got - ref)) / max(nref, 1e-30)
+    mx = float(np.abs(got - ref).max())
+    bound = MAXREL * float(np.abs(ref).max())
+    if nref == 0.0:
+        assert mx <= ZERO_REL * scale, (name, key, "expected zeros", mx, scale)
+        return 0.0
+    assert frob <= FROB and mx <= bound, (name, key, "frob", frob, "max", mx, "bound", bound)
+    return frob
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_parity(name):
+    s, coef = CASES[name]
+    inp = make_inputs(s, seed=101 + len(name))
+    dout = make_grad_output(s, seed=202 + len(name))
+    f = H.f64_inputs(inp)
+    dv = H.to_device(inp)
+    print(f"[bwd case {name}] {s} coef={coef}", flush=True)
+    got = run_train(s, dv, dout.cuda(), coef)
+    fwd = go.gqe_forward(f, s.G, s.M, s.k, s.d, s.B, s.T, shared_kv_group=s.shared_kv_group)
+    assert (got["idx"] == fwd["idx"]).all(), (name, "routing differs from the oracle's (pick another seed)")
+    ref = gb.gqe_backward(f, fwd, dout.float().numpy().astype(np.float64), s.G, s.M, s.k, s.d, s.B, s.T,
+                          shared_kv_group=s.shared_kv_group, aux_coef=coef)
+    scale = max(float(np.abs(ref[k]).max()) for k in GRADS)
+    errs = {}
+    for k in GRADS:
+        errs[k] = compare(name, k, got[k], ref[k], scale)
+    errs["dbr"] = compare(name, "dbr", got["dbr"], ref["dbr"], scale)
+    assert abs(got["aux"] - ref["aux_loss"]) <= AUX_REL * max(1.0, abs(ref["aux_loss"])), (name, got["aux"],
+                                                                                          ref["aux_loss"])
+    print(f"[bwd case {name}] frob errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+
+
+def test_backward_config2_parity():
+    """The main shape (B8 T2048 D1024 G8 M2 k1 d64) against the full oracle."""
+    s = CONFIGS[2]
+    inp = make_inputs(s, seed=1002)
+    dout = make_grad_output(s, seed=2002)
+    f = H.f64_inputs(inp)
+    dv = H.to_device(inp)
+    print(f"[bwd config 2] {s}", flush=True)
+    got = run_train(s, dv, dout.cuda(), 0.01)
+    fwd = go.gqe_forward(f, s.G, s.M, s.k, s.d, s.B, s.T)
+    same = (got["idx"] == fwd["idx"]).all(axis=(1, 2))
+    assert same.all(), ("config 2", "routing differs from the oracle on", int((~same).sum()), "tokens")
+    ref = gb.gqe_backward(f, fwd, dout.float().numpy().astype(np.float64), s.G, s.M, s.k, s.d, s.B, s.T,
+                          aux_coef=0.01)
+    scale = max(float(np.abs(ref[k]).max()) for k in GRADS)
+    for k in GRADS:
+        e = compare("config 2", k, got[k], ref[k], scale)
+        print(f"[bwd config 2] {k} frob {e:.2e}", flush=True)
+
+
+def test_backward_properties_at_32k():
+    """The 32K-token layer: bit-identical reruns (no atomics), gradients exactly
+    linear in dout under scaling by 2 (every bf16 rounding commutes with a
+    power of two), all finite."""
+    s = CONFIGS[3]
+    inp = make_inputs(s, seed=1003)
+    dv = H.to_device(inp)
+    dout = make_grad_output(s, seed=2003).cuda()
+    print(f"[bwd config 3 properties] {s}", flush=True)
+    a = run_train(s, dv, dout, 0.0)
+    b = run_train(s, dv, dout, 0.0)
+    c = run_train(s, dv, (dout.float() * 2).to(torch.bfloat16), 0.0)
+    for k in GRADS:
+        assert np.isfinite(a[k]).all(), k
+        assert np.array_equal(a[k], b[k]), (k, "rerun differs")
+        assert np.array_equal(2 * a[k], c[k]), (k, "not linear in dout")

@@ -101,6 +101,14 @@ def make_inputs(s: Shape, seed: int) -> dict:
     return out
 
 
+def make_grad_output(s: Shape, seed: int) -> torch.Tensor:
+    """Seeded gradient of the loss with respect to the layer output, [N, D]
+    N(0, 1) in the layer's storage type (the backward's synthetic input)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    return _draw(gen, (s.N, s.D), 1.0, s.torch_dtype())
+
+
 def config_inputs(cid: int) -> tuple[Shape, dict]:
     s = CONFIGS[cid]
     return s, make_inputs(s, 1000 + cid)
