@@ -8,8 +8,9 @@ one batch of seeded synthetic input already resident in HBM. The default
 workload is the 32K-token long-context layer (B=1, T=32768, D=1024, G=8, M=2,
 k=1, d_h=64, bf16). Prints ONE JSON line with tokens/s, the attention kernel's
 MFMA roofline fraction (timed live with HIP events on the library's stream),
-the speedup over dense 16q/8kv GQA built from the same kernels, and the fp64
-oracle timed on the host's cores (a baseline only).
+the speedup over dense 16q/8kv GQA built from the same kernels, the training
+step (forward that keeps its state + backward, with the attention backward's
+MFMA rate), and the fp64 oracle timed on the host's cores (a baseline only).
 """
 from __future__ import annotations
 
@@ -47,6 +48,66 @@ def layer_flops(s) -> float:
     per_tok = (2 * s.D * s.G * s.M + 2 * s.D * active_heads(s) * s.d + 4 * s.D * s.G * s.d
                + 2 * s.slots * s.d * s.D + 2 * s.G * s.k * s.d)
     return s.N * per_tok + attn_flops(s, active_heads(s))
+
+
+def attn_bwd_flops(s, heads: int) -> float:
+    """Algorithmic flops of the attention backward: five products of 2*d flops
+    per causal (query, key) pair (scores recomputed, dP, dV, dK, dQ), i.e.
+    2.5 times the forward's."""
+    return 2.5 * attn_flops(s, heads)
+
+
+def train_leg(gq, torch, s, dv, steps, warmup, mk_events):
+    """Training step = gqe_attn_fwd_train + gqe_attn_bwd on the same inputs
+    (dout seeded, resident in HBM). Returns the record's "backward" object."""
+    from workloads import make_grad_output
+    shape = gq.shape_from(s)
+    wst = torch.empty(gq.gqe_train_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty(s.N, s.D, dtype=torch.bfloat16, device="cuda")
+    dout = make_grad_output(s, seed=3000).cuda()
+    g = {k: torch.empty_like(dv[k[1:]] if k != "dx" else dv["x"], dtype=torch.float32) for k in gq.BWD_GRADS}
+    dbr = torch.empty(s.G * s.M, dtype=torch.float32, device="cuda")
+    aux = torch.empty(1, dtype=torch.float32, device="cuda")
+    coef = 0.01
+
+    def step(events=None):
+        gq.gqe_attn_fwd_train(shape, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"],
+                              dv["Wo"], out, wst)
+        gq.gqe_attn_bwd(shape, dv["x"], dv["Wr"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"], dv["Wo"], dout,
+                        coef, g, wst, dbr=dbr, aux_loss=aux, events=events)
+
+    for _ in range(warmup):
+        step()
+    # events around the two attention-backward kernels of every timed step
+    D0, D1, D2 = 3, 4, 5
+    ev = []
+    for _ in range(steps):
+        e = mk_events(3)
+        arr = [None] * (gq.GQE_BWD_N_STAGES + 1)
+        arr[D0], arr[D1], arr[D2] = e
+        ev.append((e, gq.event_array(arr)))
+    t0, t1 = mk_events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for _, arr in ev:
+        step(arr)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    dkdv_ms = sum(e[0].elapsed_time(e[1]) for e, _ in ev) / steps
+    dq_ms = sum(e[1].elapsed_time(e[2]) for e, _ in ev) / steps
+    evs = mk_events(gq.GQE_BWD_N_STAGES + 1)
+    torch.cuda.synchronize()
+    step(gq.event_array(evs))
+    torch.cuda.synchronize()
+    stage_ms = {n: round(evs[i].elapsed_time(evs[i + 1]), 4) for i, n in enumerate(gq.GQE_BWD_STAGE_NAMES)}
+    heads = active_heads(s)
+    fl = attn_bwd_flops(s, heads)
+    tf = fl / ((dkdv_ms + dq_ms) / 1e3) / 1e12
+    return {"tokens_per_s": s.N / (ms / 1e3), "ms_per_step": ms, "what": "gqe_attn_fwd_train + gqe_attn_bwd",
+            "bwd_stage_ms": stage_ms, "attn_bwd_ms": {"dkdv": dkdv_ms, "dq": dq_ms},
+            "attn_bwd_algorithmic_flops": fl, "attn_bwd_tflops": tf, "attn_bwd_frac": tf / PEAK_BF16_TFLOPS,
+            "aux_coef": coef}
 
 
 def source_sha(path: str) -> str:
@@ -118,6 +179,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gqa", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the training-step (forward + backward) leg")
     ap.add_argument("--variant", default="full", choices=["full", "weighted_concat", "hard_concat", "no_shared"],
                     help="merge of the picked experts: the layer, or one of the pages' ablations")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -225,6 +287,10 @@ def main():
                "heads": f"{s.Hq}q/{s.G}kv", "speedup_gqe_over_gqa": gqa_ms / ms_step,
                "attention_speedup": gqa_attn_ms / attn_ms}
 
+    bwd = None
+    if not args.no_backward and s.dtype == "bf16" and s.variant == "full":
+        bwd = train_leg(gq, torch, s, dv, steps, args.warmup, mk_events)
+
     peak = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
     fl = attn_flops(s, active_heads(s))
     achieved = fl / (attn_ms / 1e3) / 1e12
@@ -251,6 +317,7 @@ def main():
         "layer_mfma_frac": layer_flops(s) / (ms_step / 1e3) / 1e12 / peak,
         "stage_ms": stage_ms,
         "gqa_baseline": gqa,
+        "training_step": bwd,
         "wall_s_timed_region": wall,
         "cpu_baseline": None,
     }

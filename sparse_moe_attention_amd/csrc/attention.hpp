@@ -49,9 +49,11 @@ struct AttnArgs {
     int32_t n_o;         // row tiles per sequence of a regular group (R rows per token)
     int32_t n_x;         // row tiles per sequence of group kv1 when it carries the extra head
     int32_t o1_col;
-    // Optional (training forward): log2-domain log-sum-exp of every row,
-    // lse[row_base(g, b) + row] with row = t*Rg + r, where a sequence of a
-    // regular group spans lse_Lr rows and one of group kv1 (extra head) lse_Lx.
+    // Optional (training forward): minus the log2-domain log-sum-exp of every
+    // row, lse[row_base(g, b) + row] = -log2(sum_k exp2(s_k)) with row = t*Rg
+    // + r, where a sequence of a regular group spans lse_Lr rows and one of
+    // group kv1 (extra head) lse_Lx. Negated so that the backward's score
+    // products can start from it as their accumulator.
     float* lse;
     int64_t lse_Lr, lse_Lx;
 };
@@ -471,8 +473,8 @@ void attn_fwd_kernel(AttnArgs a) {
         const float inv = 1.f / l;
         const int rho = row0 + qb * 16 + l16;
         if (rho >= n_rows) continue;
-        // p = exp2(s - m) / l, so log2 of the normaliser is m + log2(l).
-        if (a.lse != nullptr && q4 == 0) a.lse[lse0 + rho] = __builtin_amdgcn_logf(l) - minit[qb][0];
+        // p = exp2(s - m) / l, so log2 of the normaliser is m + log2(l), m = -minit.
+        if (a.lse != nullptr && q4 == 0) a.lse[lse0 + rho] = minit[qb][0] - __builtin_amdgcn_logf(l);
         T* orow = o_row(tq[qb], rho % Rg);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {

@@ -9,8 +9,9 @@
 //   dP = dO V^T,  dS = P * (dP - delta),
 //   dV = P^T dO,  dK = dS^T q / sqrt(d),  dQ = dS K / sqrt(d).
 // Queries are stored pre-scaled, Qs = q log2(e) / sqrt(d), and the forward
-// saved lse = log2 of each row's normaliser, so P = exp2(Qs.k - lse) with
-// no per-score scaling, and dK = ln(2) * dS^T Qs.
+// saved -lse (lse = log2 of each row's normaliser), so P = exp2(Qs.k - lse)
+// with no per-score arithmetic: -lse and -delta are the accumulators the
+// score products start from. dK = ln(2) * dS^T Qs.
 //
 // Two kernels, no atomics (deterministic):
 //   * attn_bwd_dkdv_kernel: one workgroup per (group, sequence, 128 keys);
@@ -29,6 +30,8 @@
 // queries), and the matching operand is one 16-byte LDS read.
 #pragma once
 
+#include <type_traits>
+
 #include "attention.hpp"
 #include "backward.hpp"
 
@@ -39,8 +42,8 @@ struct AttnBwdArgs {
     const bf16* Qt;       // per sequence [d][L]
     const bf16* dO;       // [rows][d]
     const bf16* dOt;      // per sequence [d][L]
-    const float* lse;     // [rows], +inf on padding rows
-    const float* dlt;     // [rows]
+    const float* lse;     // [rows] -lse, -inf on padding rows
+    const float* dlt;     // [rows] -delta
     const bf16* K;        // [G][Bt][Tpad][d]
     const bf16* V;        // [G][Bt][Tpad][d], zero beyond T
     const bf16* Kt;       // [G][d][Bt*Tpad], zero beyond T
@@ -54,13 +57,45 @@ struct AttnBwdArgs {
     int32_t n_tiles;      // grid levels (key tiles / row tiles per sequence, the largest class)
 };
 
-constexpr int kBwdKW = 32;         // keys per wave (dK/dV kernel)
-constexpr int kBwdNW = 4;          // waves per dK/dV workgroup
-constexpr int kBwdBK = kBwdKW * kBwdNW;
-constexpr int kBwdQB = 64;         // query rows per step (dK/dV kernel)
-constexpr int kBwdDqNW = 8;        // waves per dQ workgroup (32 rows each)
-constexpr int kBwdDqBQ = kBwdDqNW * 32;
-constexpr int kBwdBKV = 128;       // keys per tile (dQ kernel)
+// Tile shapes (the dK/dV kernel: keys per wave, waves, query rows per
+// sub-step, waves per SIMD the registers are sized for; the dQ kernel: rows
+// per wave, waves, keys per sub-step).
+#ifndef GQE_BWD_KW
+#define GQE_BWD_KW 32
+#endif
+#ifndef GQE_BWD_NW
+#define GQE_BWD_NW 4
+#endif
+#ifndef GQE_BWD_RS
+#define GQE_BWD_RS 64
+#endif
+#ifndef GQE_BWD_WPE
+#define GQE_BWD_WPE 2
+#endif
+#ifndef GQE_BWD_DQ_QW
+#define GQE_BWD_DQ_QW 32
+#endif
+#ifndef GQE_BWD_DQ_NW
+#define GQE_BWD_DQ_NW 8
+#endif
+#ifndef GQE_BWD_DQ_KS
+#define GQE_BWD_DQ_KS 64
+#endif
+#ifndef GQE_BWD_DQ_WPE
+#define GQE_BWD_DQ_WPE 2
+#endif
+constexpr int kBwdKW = GQE_BWD_KW;         // keys per wave (dK/dV kernel)
+constexpr int kBwdNW = GQE_BWD_NW;         // waves per dK/dV workgroup
+constexpr int kBwdBK = kBwdKW * kBwdNW;    // keys per dK/dV workgroup
+constexpr int kBwdQB = 64;                 // query rows per staged step (dK/dV kernel)
+constexpr int kBwdRS = GQE_BWD_RS;         // rows per sub-step
+constexpr int kBwdDqQW = GQE_BWD_DQ_QW;    // rows per wave (dQ kernel)
+constexpr int kBwdDqNW = GQE_BWD_DQ_NW;    // waves per dQ workgroup
+constexpr int kBwdDqBQ = kBwdDqNW * kBwdDqQW;
+constexpr int kBwdBKV = 128;               // keys per staged tile (dQ kernel)
+constexpr int kBwdDqKS = GQE_BWD_DQ_KS;    // keys per sub-step
+static_assert(kBwdKW % 16 == 0 && kBwdQB % kBwdRS == 0 && kBwdRS % 32 == 0, "dK/dV tile shape");
+static_assert(kBwdDqQW % 16 == 0 && kBwdBKV % kBwdDqKS == 0 && kBwdDqKS % 32 == 0, "dQ tile shape");
 
 // Row of a 64-row step held by row i of 16-row block qb (the same order as
 // key_of_row): the 8 entries a lane holds over blocks 2j, 2j+1 are rows
@@ -68,13 +103,16 @@ constexpr int kBwdBKV = 128;       // keys per tile (dQ kernel)
 __device__ __forceinline__ int qrow_of(int qb, int i) { return key_of_row(qb, i); }
 
 template <int D>
-__global__ __launch_bounds__(kBwdNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kBwdNW * 64) __attribute__((amdgpu_waves_per_eu(GQE_BWD_WPE, GQE_BWD_WPE)))
 void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     constexpr int NT = kBwdNW * 64;
+    constexpr int KB = kBwdKW / 16;            // 16-key blocks per wave
     constexpr int DK = D / 32;                 // contraction steps over d
     constexpr int CB = D / 16;                 // 16-row blocks of dK^T / dV^T
     constexpr int QCH = D / 8;                 // 16-byte chunks per Q / dO row
     constexpr int TCH = kBwdQB / 8;            // 16-byte chunks per Q^T / dO^T row (64 rows)
+    constexpr int QBS = kBwdRS / 16;           // 16-row blocks per sub-step
+    constexpr int NSUB = kBwdQB / kBwdRS;
     constexpr int R_BYTES = kBwdQB * D * 2;    // one row-major tile
     constexpr int T_BYTES = D * kBwdQB * 2;    // one transposed tile
     constexpr int AUX = 1024;                  // lse (256 B), delta (256 B), padding
@@ -105,20 +143,20 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     // (column key = kw + 16kb + l16, contraction chunk 8*q4 of step dk).
     const bf16* Kg = a.K + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
     const bf16* Vg = a.V + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
-    Frag<bf16> kf[2][DK], vf[2][DK];
+    Frag<bf16> kf[KB][DK], vf[KB][DK];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) {
             const int64_t off = (int64_t)(kw + 16 * kb + l16) * D + dk * 32 + 8 * q4;
             kf[kb][dk] = ld_frag<bf16>(Kg + off);
             vf[kb][dk] = ld_frag<bf16>(Vg + off);
         }
-    f32x4 dkt[CB][2], dvt[CB][2];
+    f32x4 dkt[CB][KB], dvt[CB][KB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) dkt[cb][kb] = dvt[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < KB; ++kb) dkt[cb][kb] = dvt[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Steps: 64-row blocks from the first row whose token reaches k0.
     const int64_t jb0 = ((int64_t)k0 * Rg) / kBwdQB;
@@ -167,7 +205,89 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
         }
     };
 
-    auto step = [&](int j, auto st) {
+    // One sub-step of RS rows against the wave's keys; `masked` (uniform)
+    // applies the causal test, which only sub-steps whose rows reach the
+    // wave's keys need.
+    auto sub = [&](int64_t r0, int h, const char* Qs, const char* dOs, const char* Qts, const char* dOts,
+                   const char* aux, bool masked) {
+        f32x4 s[QBS][KB], dp[QBS][KB];
+        f32x4 nls[QBS], ndl[QBS];
+#pragma unroll
+        for (int qq = 0; qq < QBS; ++qq) {
+            const int qb = QBS * h + qq;
+            const int chunk = 8 * (qb >> 1) + 2 * q4 + (qb & 1);   // rows 4*chunk .. +3
+            nls[qq] = *reinterpret_cast<const f32x4*>(aux + 16 * chunk);
+            ndl[qq] = *reinterpret_cast<const f32x4*>(aux + 256 + 16 * chunk);
+        }
+        // Contraction steps outermost: dependent products stay QBS*KB*2 apart.
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk)
+#pragma unroll
+            for (int qq = 0; qq < QBS; ++qq) {
+                const int qr = qrow_of(QBS * h + qq, l16), c = 4 * dk + q4;
+                const Frag<bf16> qf = ld_frag<bf16>(Qs + k_chunk_off<QCH>(qr, c));
+                const Frag<bf16> of = ld_frag<bf16>(dOs + k_chunk_off<QCH>(qr, c));
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    s[qq][kb] = mma16(qf, kf[kb][dk], dk == 0 ? nls[qq] : s[qq][kb]);
+                    dp[qq][kb] = mma16(of, vf[kb][dk], dk == 0 ? ndl[qq] : dp[qq][kb]);
+                }
+            }
+        if (__builtin_expect(masked, false)) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                // rows of this sub-step before key*Rg (< 2^31 apart) are masked
+                const int lim = (int)((int64_t)(kw + 16 * kb + l16) * Rg - r0);
+#pragma unroll
+                for (int qq = 0; qq < QBS; ++qq)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (qrow_of(QBS * h + qq, 4 * q4 + v) < lim) s[qq][kb][v] = -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int qq = 0; qq < QBS; ++qq)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float pv = __builtin_amdgcn_exp2f(s[qq][kb][v]);
+                    s[qq][kb][v] = pv;
+                    dp[qq][kb][v] = pv * dp[qq][kb][v];
+                }
+        // P and dS fragments, 32 rows per contraction step: lane group q4
+        // holds rows 32j + 8*q4 .. +7 of key column l16.
+#pragma unroll
+        for (int jj = 0; jj < QBS / 2; ++jj) {
+            const int j32 = (QBS / 2) * h + jj;              // 32-row step within the 64 rows
+            Frag<bf16> pf[KB], sf[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    pf[kb].v[v] = (bf16)s[2 * jj][kb][v];
+                    pf[kb].v[4 + v] = (bf16)s[2 * jj + 1][kb][v];
+                    sf[kb].v[v] = (bf16)dp[2 * jj][kb][v];
+                    sf[kb].v[4 + v] = (bf16)dp[2 * jj + 1][kb][v];
+                }
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int c = cb * 16 + l16, ch = 4 * j32 + q4;
+                const Frag<bf16> of = ld_frag<bf16>(dOts + v_chunk_off<TCH>(c, ch));
+                const Frag<bf16> qf = ld_frag<bf16>(Qts + v_chunk_off<TCH>(c, ch));
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    dvt[cb][kb] = mma16(of, pf[kb], dvt[cb][kb]);
+                    dkt[cb][kb] = mma16(qf, sf[kb], dkt[cb][kb]);
+                }
+            }
+        }
+    };
+
+    // One staged step. Edge steps (rows whose tokens reach the workgroup's
+    // keys) test each sub-step for keys after every row (skip) or after some
+    // row (causal mask); the others need neither and run branch-free.
+    auto step = [&](int j, auto st, auto edge) {
         constexpr int SI = decltype(st)::value;
         if (j + 1 < n_steps) dma(j + 1, StageC<SI ^ 1>{});
         const int64_t r0 = (jb0 + j) * kBwdQB;
@@ -178,83 +298,35 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
         const char* dOts = Qts + T_BYTES;
         const char* aux = dOts + T_BYTES;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {          // rows 32h .. 32h+31 of the step
-            const int64_t rlo = r0 + 32 * h;
-            const int t_lo = (int)(rlo / Rg), t_hi = (int)((rlo + 31) / Rg);
-            if (kw > t_hi || rlo >= Lreal) continue;          // every key after every row's token
-            f32x4 s[2][2], dp[2][2];                           // [qb of the half][kb]
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                const int qb = 2 * h + qq;
-                const int chunk = 8 * (qb >> 1) + 2 * q4 + (qb & 1);   // rows 4*chunk .. +3
-                const f32x4 ls = *reinterpret_cast<const f32x4*>(aux + 16 * chunk);
-                const f32x4 dl = *reinterpret_cast<const f32x4*>(aux + 256 + 16 * chunk);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    s[qq][kb] = -ls;
-                    dp[qq][kb] = -dl;
-                }
-                const int qr = qrow_of(qb, l16);
-#pragma unroll
-                for (int dk = 0; dk < DK; ++dk) {
-                    const int c = 4 * dk + q4;
-                    const Frag<bf16> qf = ld_frag<bf16>(Qs + k_chunk_off<QCH>(qr, c));
-                    const Frag<bf16> of = ld_frag<bf16>(dOs + k_chunk_off<QCH>(qr, c));
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        s[qq][kb] = mma16(qf, kf[kb][dk], s[qq][kb]);
-                        dp[qq][kb] = mma16(of, vf[kb][dk], dp[qq][kb]);
-                    }
-                }
-            }
-            const bool mask = kw + kBwdKW - 1 > t_lo;
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float x = s[qq][kb][v];
-                        if (mask) {
-                            const int64_t rho = r0 + qrow_of(2 * h + qq, 4 * q4 + v);
-                            if (kw + 16 * kb + l16 > (int)(rho / Rg)) x = -INFINITY;
-                        }
-                        const float pv = __builtin_amdgcn_exp2f(x);
-                        s[qq][kb][v] = pv;
-                        dp[qq][kb][v] = pv * dp[qq][kb][v];
-                    }
-            // P and dS fragments: lane group q4 holds rows 32h + 8*q4 .. +7 of key column l16.
-            Frag<bf16> pf[2], sf[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    pf[kb].v[v] = (bf16)s[0][kb][v];
-                    pf[kb].v[4 + v] = (bf16)s[1][kb][v];
-                    sf[kb].v[v] = (bf16)dp[0][kb][v];
-                    sf[kb].v[4 + v] = (bf16)dp[1][kb][v];
-                }
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const int c = cb * 16 + l16, ch = 4 * h + q4;
-                const Frag<bf16> of = ld_frag<bf16>(dOts + v_chunk_off<TCH>(c, ch));
-                const Frag<bf16> qf = ld_frag<bf16>(Qts + v_chunk_off<TCH>(c, ch));
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    dvt[cb][kb] = mma16(of, pf[kb], dvt[cb][kb]);
-                    dkt[cb][kb] = mma16(qf, sf[kb], dkt[cb][kb]);
-                }
+        for (int h = 0; h < NSUB; ++h) {       // rows RS*h .. RS*h + RS-1 of the step
+            if constexpr (decltype(edge)::value) {
+                // Row rho belongs to token floor(rho / Rg), and key > floor(rho / Rg)
+                // exactly when rho < key * Rg: the causal tests need no division.
+                const int64_t rlo = r0 + kBwdRS * h;
+                if (rlo + kBwdRS - 1 < (int64_t)kw * Rg || rlo >= Lreal) continue;   // every key after every row's token
+                sub(r0, h, Qs, dOs, Qts, dOts, aux, rlo < (int64_t)(kw + kBwdKW - 1) * Rg);
+            } else {
+                sub(r0, h, Qs, dOs, Qts, dOts, aux, false);
             }
         }
         __syncthreads();
     };
 
     if (n_steps > 0) {
+        // Steps whose first row lies before the last key's first row are edge
+        // steps; an even count keeps the two LDS stages in step with j.
+        const int64_t thr = (int64_t)(k0 + kBwdBK - 1) * Rg;
+        int jm = (int)min<int64_t>(n_steps, max<int64_t>(0, (thr + kBwdQB - 1) / kBwdQB - jb0));
+        jm += jm & 1;
         dma(0, StageC<0>{});
         __syncthreads();
-        for (int j = 0; j < n_steps; j += 2) {
-            step(j, StageC<0>{});
-            if (j + 1 < n_steps) step(j + 1, StageC<1>{});
+        for (int j = 0; j < jm; j += 2) {
+            step(j, StageC<0>{}, std::true_type{});
+            if (j + 1 < n_steps) step(j + 1, StageC<1>{}, std::true_type{});
+        }
+        for (int j = jm; j < n_steps; j += 2) {
+            step(j, StageC<0>{}, std::false_type{});
+            if (j + 1 < n_steps) step(j + 1, StageC<1>{}, std::false_type{});
         }
     }
 
@@ -262,7 +334,7 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     // columns 16cb + 4*q4 .. +3.
     constexpr float kLn2 = 0.69314718055994531f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
         const int key = kw + 16 * kb + l16;
         if (key >= T_) continue;
         bf16* row = a.dY + ((int64_t)b * T_ + key) * a.ldy;
@@ -282,10 +354,12 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kBwdDqNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kBwdDqNW * 64) __attribute__((amdgpu_waves_per_eu(GQE_BWD_DQ_WPE, GQE_BWD_DQ_WPE)))
 void attn_bwd_dq_kernel(AttnBwdArgs a) {
     constexpr int NT = kBwdDqNW * 64;
     constexpr int BKV = kBwdBKV;
+    constexpr int QBW = kBwdDqQW / 16;         // 16-row blocks per wave
+    constexpr int KBS = kBwdDqKS / 16;         // 16-key blocks per sub-step
     constexpr int DK = D / 32;
     constexpr int CB = D / 16;
     constexpr int KCH = D / 8;                 // chunks per K / V row
@@ -313,33 +387,35 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
     const int qt = n_t - 1 - lv;
     if (qt < 0) return;
     const int64_t base = rs_base(a.rs, g, b);
-    const int64_t row0 = (int64_t)qt * kBwdDqBQ + wave * 32;    // first row of this wave
+    const int64_t row0 = (int64_t)qt * kBwdDqBQ + wave * kBwdDqQW;    // first row of this wave
 
     const bf16* Qb = a.Q + base * D;
     const bf16* dOb = a.dO + base * D;
-    Frag<bf16> qf[2][DK], of[2][DK];
-    float nls[2], ndl[2];
-    int tq[2];
+    Frag<bf16> qf[QBW][DK], of[QBW][DK];
+    float nls[QBW], ndl[QBW];     // -lse, -delta of the lane's row (the score products' start)
+    int tq[QBW];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QBW; ++qb) {
         const int64_t rho = row0 + 16 * qb + l16;               // < L: padding rows are readable
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) {
             qf[qb][dk] = ld_frag<bf16>(Qb + rho * D + dk * 32 + 8 * q4);
             of[qb][dk] = ld_frag<bf16>(dOb + rho * D + dk * 32 + 8 * q4);
         }
-        nls[qb] = -a.lse[base + rho];
-        ndl[qb] = -a.dlt[base + rho];
+        nls[qb] = a.lse[base + rho];
+        ndl[qb] = a.dlt[base + rho];
         tq[qb] = (int)(rho / Rg);
     }
     const int t_first = (int)(row0 / Rg);
-    const int t_last = (int)min<int64_t>(T_ - 1, (row0 + 31) / Rg);
+    const int t_last = (int)min<int64_t>(T_ - 1, (row0 + kBwdDqQW - 1) / Rg);
     const int t_tile = (int)min<int64_t>(T_ - 1, ((int64_t)qt * kBwdDqBQ + kBwdDqBQ - 1) / Rg);
     const int n_kv = t_tile / BKV + 1;
 
-    f32x4 dqt[CB][2];
+    f32x4 dqt[CB][QBW];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) dqt[cb][0] = dqt[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) dqt[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int64_t vrow = (int64_t)a.rs.Bt * a.Tpad;
     const bf16* Kg = a.K + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
@@ -374,7 +450,65 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
                                              (__attribute__((address_space(3))) void*)(S + 2 * K_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
     };
 
-    auto tile = [&](int j, auto st) {
+    // One sub-step of KS keys against the wave's rows; `masked` (uniform)
+    // applies the causal test.
+    auto sub = [&](int k0, int h, const char* Ks, const char* Vs, const char* Kts, bool masked) {
+        f32x4 s[KBS][QBW], dp[KBS][QBW];
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk)
+#pragma unroll
+            for (int kb = 0; kb < KBS; ++kb) {
+                const int kr = key_of_row(KBS * h + kb, l16), c = 4 * dk + q4;
+                const Frag<bf16> kfr = ld_frag<bf16>(Ks + k_chunk_off<KCH>(kr, c));
+                const Frag<bf16> vfr = ld_frag<bf16>(Vs + k_chunk_off<KCH>(kr, c));
+#pragma unroll
+                for (int qb = 0; qb < QBW; ++qb) {
+                    const f32x4 c0 = {nls[qb], nls[qb], nls[qb], nls[qb]}, c1 = {ndl[qb], ndl[qb], ndl[qb], ndl[qb]};
+                    s[kb][qb] = mma16(kfr, qf[qb][dk], dk == 0 ? c0 : s[kb][qb]);
+                    dp[kb][qb] = mma16(vfr, of[qb][dk], dk == 0 ? c1 : dp[kb][qb]);
+                }
+            }
+        if (__builtin_expect(masked, false)) {
+#pragma unroll
+            for (int kb = 0; kb < KBS; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QBW; ++qb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (k0 + key_of_row(KBS * h + kb, 4 * q4 + v) > tq[qb]) s[kb][qb][v] = -INFINITY;
+        }
+#pragma unroll
+        for (int kb = 0; kb < KBS; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < QBW; ++qb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    s[kb][qb][v] = __builtin_amdgcn_exp2f(s[kb][qb][v]) * dp[kb][qb][v];
+        // dS^T fragments: lane q4 holds keys 32kc + 8*q4 .. +7 of query l16.
+#pragma unroll
+        for (int kk = 0; kk < KBS / 2; ++kk) {
+            const int kc = (KBS / 2) * h + kk;              // 32-key step within the tile
+            Frag<bf16> sf[QBW];
+#pragma unroll
+            for (int qb = 0; qb < QBW; ++qb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    sf[qb].v[v] = (bf16)s[2 * kk][qb][v];
+                    sf[qb].v[4 + v] = (bf16)s[2 * kk + 1][qb][v];
+                }
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const Frag<bf16> ktf = ld_frag<bf16>(Kts + v_chunk_off<VCH>(cb * 16 + l16, 4 * kc + q4));
+#pragma unroll
+                for (int qb = 0; qb < QBW; ++qb) dqt[cb][qb] = mma16(ktf, sf[qb], dqt[cb][qb]);
+            }
+        }
+    };
+
+    // One staged key tile. Edge tiles (keys that reach the workgroup's first
+    // token) test each sub-step for keys after every row of the wave (skip)
+    // or after some row (causal mask); the others run branch-free.
+    auto tile = [&](int j, auto st, auto edge) {
         constexpr int SI = decltype(st)::value;
         if (j + 1 < n_kv) dma(j + 1, StageC<SI ^ 1>{});
         const int k0 = j * BKV;
@@ -382,74 +516,38 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
         const char* Vs = Ks + K_BYTES;
         const char* Kts = Vs + K_BYTES;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {          // keys 64h .. 64h+63 of the tile
-            const int kh = k0 + 64 * h;
-            if (kh > t_last) continue;
-            f32x4 s[4][2], dp[4][2];            // [kb of the half][qb]
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                s[kb][0] = f32x4{nls[0], nls[0], nls[0], nls[0]};
-                s[kb][1] = f32x4{nls[1], nls[1], nls[1], nls[1]};
-                dp[kb][0] = f32x4{ndl[0], ndl[0], ndl[0], ndl[0]};
-                dp[kb][1] = f32x4{ndl[1], ndl[1], ndl[1], ndl[1]};
-            }
-#pragma unroll
-            for (int dk = 0; dk < DK; ++dk)
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const int kr = key_of_row(4 * h + kb, l16), c = 4 * dk + q4;
-                    const Frag<bf16> kfr = ld_frag<bf16>(Ks + k_chunk_off<KCH>(kr, c));
-                    const Frag<bf16> vfr = ld_frag<bf16>(Vs + k_chunk_off<KCH>(kr, c));
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
-                        s[kb][qb] = mma16(kfr, qf[qb][dk], s[kb][qb]);
-                        dp[kb][qb] = mma16(vfr, of[qb][dk], dp[kb][qb]);
-                    }
-                }
-            const bool mask = kh + 63 > t_first;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float x = s[kb][qb][v];
-                        if (mask && k0 + key_of_row(4 * h + kb, 4 * q4 + v) > tq[qb]) x = -INFINITY;
-                        s[kb][qb][v] = __builtin_amdgcn_exp2f(x) * dp[kb][qb][v];
-                    }
-            // dS^T fragments: lane q4 holds keys 32kc + 8*q4 .. +7 (kc = 2h + kk) of query l16.
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                Frag<bf16> sf[2];
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        sf[qb].v[v] = (bf16)s[2 * kk][qb][v];
-                        sf[qb].v[4 + v] = (bf16)s[2 * kk + 1][qb][v];
-                    }
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const Frag<bf16> ktf = ld_frag<bf16>(Kts + v_chunk_off<VCH>(cb * 16 + l16, 4 * (2 * h + kk) + q4));
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) dqt[cb][qb] = mma16(ktf, sf[qb], dqt[cb][qb]);
-                }
+        for (int h = 0; h < BKV / kBwdDqKS; ++h) {     // keys KS*h .. KS*h + KS-1 of the tile
+            if constexpr (decltype(edge)::value) {
+                const int kh = k0 + kBwdDqKS * h;
+                if (kh > t_last) continue;
+                sub(k0, h, Ks, Vs, Kts, kh + kBwdDqKS - 1 > t_first);   // a key may lie above a row's token
+            } else {
+                sub(k0, h, Ks, Vs, Kts, false);
             }
         }
         __syncthreads();
     };
 
+    // Tiles whose keys all precede the workgroup's first token need no causal
+    // test; an even count keeps the two LDS stages in step with j.
+    const int t_wg = (int)(((int64_t)qt * kBwdDqBQ) / Rg);
+    int n_um = min(n_kv, (t_wg + 1) / BKV);
+    n_um -= n_um & 1;
     dma(0, StageC<0>{});
     __syncthreads();
-    for (int j = 0; j < n_kv; j += 2) {
-        tile(j, StageC<0>{});
-        if (j + 1 < n_kv) tile(j + 1, StageC<1>{});
+    for (int j = 0; j < n_um; j += 2) {
+        tile(j, StageC<0>{}, std::false_type{});
+        tile(j + 1, StageC<1>{}, std::false_type{});
+    }
+    for (int j = n_um; j < n_kv; j += 2) {
+        tile(j, StageC<0>{}, std::true_type{});
+        if (j + 1 < n_kv) tile(j + 1, StageC<1>{}, std::true_type{});
     }
 
     // dq = dS K / sqrt(d): lane holds row row0 + 16qb + l16, columns 16cb + 4*q4 .. +3.
     const float sc = 1.f / sqrtf((float)D);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QBW; ++qb) {
         const int64_t rho = row0 + 16 * qb + l16;
         if (rho >= Lreal) continue;
         const int t = tq[qb], r = (int)(rho - (int64_t)t * Rg);

@@ -97,8 +97,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
 //   shared row:         dO = dC_shared;
 // and delta = <dO, O> (with the bf16 dO the attention kernels use). Writes
 // Q and dO row-major (rows of the row space) and transposed ([d][rows] per
-// sequence), delta, and for padding rows zero Q / dO / delta and lse = +inf,
-// so the attention kernels read whole tiles without tests.
+// sequence), -delta, and for padding rows zero Q / dO / delta and a negated
+// log-sum-exp of -inf (probability 0), so the attention kernels read whole
+// tiles without tests.
 // Grid: (row blocks of 64, G*Bt). 256 threads; d/8 lanes per row.
 // ---------------------------------------------------------------------------
 struct PrepArgs {
@@ -111,8 +112,8 @@ struct PrepArgs {
     bf16* Qt;             // per sequence [d][L]
     bf16* dOc;
     bf16* dOt;
-    float* lse;           // [rows] (padding rows set here)
-    float* dlt;           // [rows]
+    float* lse;           // [rows] minus the log2 log-sum-exp (padding rows set here)
+    float* dlt;           // [rows] minus delta
     float* dw;            // [N, G*k]
     RowSpace rs;
     int64_t ldc;
@@ -178,8 +179,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             s_dl += __shfl_xor(s_dl, m);
         }
         if (cc == 0) {
-            a.dlt[base + rho] = s_dl;
-            if (!real) a.lse[base + rho] = INFINITY;
+            a.dlt[base + rho] = -s_dl;
+            if (!real) a.lse[base + rho] = -INFINITY;
             else if (r < a.k) a.dw[n * GK + g * a.k + r] = s_dw;
         }
         store8(a.Qc + (base + rho) * a.d + 8 * cc, q);

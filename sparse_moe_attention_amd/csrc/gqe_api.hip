@@ -321,7 +321,7 @@ struct TrainWs {
     size_t lse, dlt, Qc, Qt, dOc, dOt, dw, dz, p, cs, dC, WoT, WcT, xT, doT, CT, Kt, V, dY, dYt, part, total;
 };
 
-constexpr int kRowPad = kBwdDqBQ;    // row-space runs pad to whole dQ row tiles
+constexpr int kRowPad = kBwdDqBQ > 256 ? kBwdDqBQ : 256;   // row-space runs pad to whole dQ row tiles
 constexpr int kColsumRows = 1024;
 
 // Splits of a weight-gradient GEMM over its token contraction: about 1024
