@@ -258,6 +258,42 @@ gqe_status gqe_attn_bwd_timed(const gqe_shape* s, const void* x, const void* Wr,
                               float* aux_loss, void* ws, size_t ws_bytes, void* stream,
                               void* const* events);
 
+/* ---------------------------------------------------------------------------
+ * Decode: one new token per sequence over a dense KV cache. GQE keeps the K/V
+ * projections, and so the KV cache, of the underlying GQA model unchanged;
+ * only the query side is sparse ([GQE-x] "Architecture and routing"; [GQE-n]
+ * part 4). Full layer (GQE_FULL), bf16.
+ *   s          B sequences; T = cache capacity per sequence (a multiple of 32);
+ *              D, G, M, k, d_h, shared_kv_group as for the layer
+ *   pos        [B] int32, device: sequence b has pos[b] cached positions and the
+ *              new token goes at position pos[b] (0 <= pos[b] < T; an entry
+ *              outside that range leaves its cache untouched and its outputs
+ *              unspecified, with no out-of-bounds access)
+ *   x          [B, D] bf16 new tokens; weights as in gqe_attn_fwd
+ *   k_cache    [G][B][T][d_h] bf16, in/out: keys; row pos[b] is written
+ *   vt_cache   [G][d_h][B*T] bf16, in/out: values transposed (element
+ *              (g, c, b*T + t) is value c of position t); column b*T + pos[b]
+ *              is written. Positions past pos[b] are never read as data.
+ *   out        [B, D] bf16; idx_out, w_out [B, G, k] optional as in gqe_attn_fwd
+ * The layouts are those the prefill uses for K and V^T, so a cache can be
+ * filled by projecting a prompt with the same weights. */
+size_t gqe_decode_workspace_bytes(const gqe_shape* s);
+gqe_status gqe_decode_step(const gqe_shape* s, const int32_t* pos, const void* x, const void* Wr,
+                           const float* br, const void* Wq, const void* Wk, const void* Wv,
+                           const void* Wq_sh, const void* Wo, void* k_cache, void* vt_cache, void* out,
+                           int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Instrumented gqe_decode_step (events as for gqe_attn_fwd_timed,
+ * GQE_DECODE_N_STAGES+1 entries). Stages: 0 new-token projections, routing,
+ * sparse Q and cache append; 1 attention over the cache; 2 chunk merge,
+ * merged slots and output projection. */
+#define GQE_DECODE_N_STAGES 3
+gqe_status gqe_decode_step_timed(const gqe_shape* s, const int32_t* pos, const void* x, const void* Wr,
+                                 const float* br, const void* Wq, const void* Wk, const void* Wv,
+                                 const void* Wq_sh, const void* Wo, void* k_cache, void* vt_cache,
+                                 void* out, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                                 void* stream, void* const* events);
+
 /* A static, NUL-terminated description of a status code. */
 const char* gqe_status_str(gqe_status st);
 

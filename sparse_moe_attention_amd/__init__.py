@@ -14,6 +14,8 @@ Entry points (same names as the C ABI in include/gqe.h):
     gqe_train_workspace_bytes(shape)
     gqe_attn_fwd_train(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, ws, idx_out=None, w_out=None)
     gqe_attn_bwd(shape, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, grads, ws, dbr=None, aux_loss=None)
+    gqe_decode_workspace_bytes(shape)
+    gqe_decode_step(shape, pos, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, k_cache, vt_cache, out, ws, idx_out=None, w_out=None)
     gqe_status_str(code)
 """
 from __future__ import annotations
@@ -36,6 +38,8 @@ GQA_STAGE_NAMES = ("proj_qkv", "attention", "out_proj")
 GQE_BWD_N_STAGES = 7
 GQE_BWD_STAGE_NAMES = ("layouts", "slot_grads_dWo", "prep_router", "attn_dkdv", "attn_dq", "dx",
                        "dW")
+GQE_DECODE_N_STAGES = 3
+GQE_DECODE_STAGE_NAMES = ("token_side_and_append", "attention_over_cache", "merge_and_out_proj")
 # Gradient outputs of gqe_attn_bwd, in argument order (fp32, shaped like the weights).
 BWD_GRADS = ("dx", "dWr", "dWq", "dWk", "dWv", "dWq_sh", "dWo")
 
@@ -101,6 +105,13 @@ def load() -> ctypes.CDLL:
     lib.gqe_attn_bwd.restype = ctypes.c_int
     lib.gqe_attn_bwd_timed.argtypes = bwd + [P]
     lib.gqe_attn_bwd_timed.restype = ctypes.c_int
+    lib.gqe_decode_workspace_bytes.argtypes = [SH]
+    lib.gqe_decode_workspace_bytes.restype = S
+    dec = [SH, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gqe_decode_step.argtypes = dec
+    lib.gqe_decode_step.restype = ctypes.c_int
+    lib.gqe_decode_step_timed.argtypes = dec + [P]
+    lib.gqe_decode_step_timed.restype = ctypes.c_int
     lib.gqe_status_str.argtypes = [ctypes.c_int]
     lib.gqe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -250,3 +261,23 @@ def gqe_attn_bwd(shape, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, grads, ws,
         _check(lib.gqe_attn_bwd(*args))
     else:
         _check(lib.gqe_attn_bwd_timed(*args, events))
+
+
+def gqe_decode_workspace_bytes(shape: GqeShape) -> int:
+    """Workspace of gqe_decode_step (shape.T = cache capacity; 0: unsupported)."""
+    return int(load().gqe_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def gqe_decode_step(shape, pos, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, k_cache, vt_cache, out, ws, idx_out=None,
+                    w_out=None, stream=None, events=None):
+    """One new token per sequence over the dense KV cache (appends the token's
+    key and value at pos[b]); events: optional ctypes array of
+    GQE_DECODE_N_STAGES + 1 entries."""
+    lib = load()
+    args = [ctypes.byref(shape), _ptr(pos), _ptr(x), _ptr(Wr), _ptr(br), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wq_sh),
+            _ptr(Wo), _ptr(k_cache), _ptr(vt_cache), _ptr(out), _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel(),
+            _stream(stream)]
+    if events is None:
+        _check(lib.gqe_decode_step(*args))
+    else:
+        _check(lib.gqe_decode_step_timed(*args, events))

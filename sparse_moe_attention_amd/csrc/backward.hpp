@@ -235,8 +235,8 @@ struct RouterBwdArgs {
     float coef;
 };
 
-__global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(64) void router_bwd_kernel(RouterBwdArgs a) {
+    const int64_t n = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (n >= a.N) return;
     const int E = a.G * a.M, GK = a.G * a.k;
     const float* lg = a.logits + n * E;
@@ -295,17 +295,30 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
 }
 
 // Column sums of two [N, E] fp32 matrices over a block of rows each:
-// part[blk][e] and part[nblk + blk][e]. Rows in order: deterministic.
+// part[blk][e] and part[nblk + blk][e]. The G = 256 / E row lanes of a
+// column (G*E threads) read interleaved rows, so every pass reads G whole
+// consecutive rows; the lanes' sums are then added in lane order (fixed
+// order: deterministic).
 __global__ __launch_bounds__(256) void colsum_kernel(const float* a, const float* b, float* part, int64_t N, int E,
                                                      int rows_per_blk) {
+    __shared__ float red[256];
+    const int G = 256 / E;                     // row lanes per column (E <= 256)
+    const int tid = threadIdx.x, e = tid % E, lr = tid / E;
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_blk;
     const int64_t r1 = min<int64_t>(N, r0 + rows_per_blk);
-    for (int u = threadIdx.x; u < 2 * E; u += blockDim.x) {
-        const float* src = u < E ? a : b;
-        const int e = u < E ? u : u - E;
+    for (int m = 0; m < 2; ++m) {
+        const float* src = m == 0 ? a : b;
         float s = 0.f;
-        for (int64_t r = r0; r < r1; ++r) s += src[r * E + e];
-        part[((u < E ? 0 : gridDim.x) + blockIdx.x) * (int64_t)E + e] = s;
+        if (lr < G)
+            for (int64_t r = r0 + lr; r < r1; r += G) s += src[r * E + e];
+        red[tid] = s;
+        __syncthreads();
+        if (tid < E) {
+            float t = 0.f;
+            for (int i = 0; i < G; ++i) t += red[i * E + tid];
+            part[((int64_t)m * gridDim.x + blockIdx.x) * E + tid] = t;
+        }
+        __syncthreads();
     }
 }
 

@@ -1,0 +1,241 @@
+// One decode step of the GQE layer over a dense KV cache: one new token per
+// sequence. The K/V projections and the cache are those of the underlying
+// GQA model, unchanged; only the query side is sparse ("Grouped Query
+// Experts" explainer, technical summary, "Architecture and routing";
+// FrontiersMind GQE article, part 4). Reading the cache dominates, so the
+// attention kernel is an HBM stream:
+//   * append_kernel: the new token's key row and value column into the cache;
+//   * attn_decode_kernel: one workgroup per (sequence, group, chunk of cached
+//     keys); each wave streams its keys straight from HBM into MFMA operands
+//     (K rows as the A operand of S^T = K Q^T, V^T rows as the A operand of
+//     O^T = V^T P^T) for all query heads of the group at once (the picked
+//     experts and, on its group, the shared head, zero-padded to 16), with an
+//     online softmax, and writes the chunk's (max, sum, unnormalised output);
+//   * decode_combine_kernel: merges the chunks of every head, then writes the
+//     merged slots C = [hard | weighted | shared] for the output projection.
+// The cache layout is the prefill's: keys [G][B][T][d] (one contiguous row
+// per key), values transposed [G][d][B*T] (contiguous keys per column).
+#pragma once
+
+#include "attention.hpp"
+
+namespace gqe {
+
+// k_cache[g][b][pos[b]] = Kn[b][g], vt_cache[g][c][b*T + pos[b]] = Vn[b][g][c].
+// Grid B*G, 64 threads (d <= 64).
+__global__ __launch_bounds__(64) void append_kernel(const bf16* Kn, const bf16* Vn, const int32_t* pos, bf16* kc,
+                                                    bf16* vtc, int64_t T, int Bt, int G, int d) {
+    const int b = blockIdx.x / G, g = blockIdx.x % G, c = threadIdx.x;
+    if (c >= d) return;
+    const int64_t p = pos[b];
+    if (p < 0 || p >= T) return;    // refused on the host when it can be checked; never written
+    const int64_t src = ((int64_t)b * G + g) * d + c;
+    kc[(((int64_t)g * Bt + b) * T + p) * d + c] = Kn[src];
+    vtc[((int64_t)g * d + c) * ((int64_t)Bt * T) + (int64_t)b * T + p] = Vn[src];
+}
+
+struct DecodeArgs {
+    const bf16* Qr;       // [B, G*k, d] routed queries (pre-scaled by log2(e)/sqrt(d))
+    const bf16* Qsh;      // [B, d] shared-head query (pre-scaled)
+    const bf16* K;        // [G][B][T][d]
+    const bf16* Vt;       // [G][d][B*T]
+    const int32_t* pos;   // [B]: the new token sits at pos[b]; keys 0 .. pos[b] are attended
+    float* part_o;        // [B][G][n_ch][R16][d] unnormalised outputs (relative to part_m)
+    float* part_ml;       // [B][G][n_ch][R16][2] (max, sum) in log2 units
+    int64_t T;
+    int32_t Bt, G, k, s0, d;
+    int32_t n_ch;         // chunks per sequence
+    int32_t R16;          // head slots per group, a multiple of 16 (>= k + 1)
+};
+
+constexpr int kDecNW = 4;          // waves per workgroup
+constexpr int kDecCW = 256;        // keys per wave
+constexpr int kDecCH = kDecNW * kDecCW;
+
+template <int D>
+__global__ __launch_bounds__(kDecNW * 64) void attn_decode_kernel(DecodeArgs a) {
+    constexpr int DK = D / 32, CB = D / 16;
+    constexpr int NB = kDecCW / 32;                 // 32-key steps per wave
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int ch = blockIdx.x % a.n_ch;
+    const int bg = blockIdx.x / a.n_ch, g = bg % a.G, b = bg / a.G;
+    const int64_t p = a.pos[b];
+    if (p < 0 || p >= a.T) return;                  // not a cache position: nothing is read
+    const int64_t len = p + 1;                      // keys 0 .. pos[b]
+    const int64_t c0 = (int64_t)ch * kDecCH;
+    if (c0 >= len) return;                          // the combine reads chunks below len only
+    const int Rg = a.k + (g == a.s0 ? 1 : 0);
+    const bf16* Kg = a.K + ((int64_t)g * a.Bt + b) * a.T * D;
+    const int64_t vrow = (int64_t)a.Bt * a.T;
+    const bf16* Vg = a.Vt + (int64_t)g * D * vrow + (int64_t)b * a.T;
+
+    __shared__ float s_m[kDecNW][16], s_l[kDecNW][16];
+    __shared__ float s_o[kDecNW][D][16];
+
+    for (int h0 = 0; h0 < Rg; h0 += 16) {           // 16 heads per pass (one pass unless k >= 16)
+        // Queries as the B operand: column l16 = head h0 + l16 (zero beyond Rg).
+        Frag<bf16> qf[DK];
+        const int hd = h0 + l16;
+        const bf16* qp = hd < a.k ? a.Qr + ((int64_t)b * a.G * a.k + (int64_t)g * a.k + hd) * D
+                                  : (hd < Rg ? a.Qsh + (int64_t)b * D : nullptr);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            if (qp != nullptr) qf[dk] = ld_frag<bf16>(qp + dk * 32 + 8 * q4);
+            else qf[dk].v = bf16x8{};
+        }
+        Frag<bf16> ones;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ones.v[i] = (bf16)(l16 == 0 ? 1.f : 0.f);
+        f32x4 o[CB], lsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY;                         // running max of head l16 (log2 units)
+
+        const int64_t w0 = c0 + (int64_t)wave * kDecCW;
+        const int nb = (int)max<int64_t>(0, min<int64_t>(NB, (len - w0 + 31) / 32));
+        // Operand fragments of one 32-key step: K rows (A of S^T) and V^T rows (A of O^T).
+        auto load = [&](int j, Frag<bf16> (&kf)[2][DK], Frag<bf16> (&vf)[CB]) {
+            const int64_t k0 = w0 + 32 * j;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int dk = 0; dk < DK; ++dk)
+                    kf[kb][dk] = ld_frag<bf16>(Kg + (k0 + key_of_row(kb, l16)) * D + dk * 32 + 8 * q4);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) vf[cb] = ld_frag<bf16>(Vg + (int64_t)(cb * 16 + l16) * vrow + k0 + 8 * q4);
+        };
+        Frag<bf16> kA[2][DK], vA[CB], kB[2][DK], vB[CB];
+        auto compute = [&](int j, const Frag<bf16> (&kf)[2][DK], const Frag<bf16> (&vfin)[CB]) {
+            const int64_t k0 = w0 + 32 * j;
+            f32x4 s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int dk = 0; dk < DK; ++dk) s[kb] = mma16(kf[kb][dk], qf[dk], s[kb]);
+            }
+            Frag<bf16> vf[CB];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) vf[cb] = vfin[cb];
+            if (k0 + 32 > len) {
+                // Keys at or past len are not attended: their scores become -inf
+                // and their values 0 (the cache there may hold any bits, and a
+                // NaN times a zero probability would still be NaN).
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (k0 + key_of_row(kb, 4 * q4 + v) >= len) s[kb][v] = -INFINITY;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (k0 + 8 * q4 + i >= len) vf[cb].v[i] = (bf16)0.f;
+            }
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) mx = vmax(mx, s[kb][v]);
+            mx = quad_row_max(mx);
+            const float mn = vmax(m, mx);
+            const float corr = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first step (m = -inf)
+            m = mn;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) o[cb] *= corr;
+            lsum *= corr;
+            Frag<bf16> pf;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                pf.v[v] = (bf16)__builtin_amdgcn_exp2f(s[0][v] - mn);
+                pf.v[4 + v] = (bf16)__builtin_amdgcn_exp2f(s[1][v] - mn);
+            }
+            lsum = mma16(ones, pf, lsum);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) o[cb] = mma16(vf[cb], pf, o[cb]);
+        };
+        // Two register sets: the next step's loads are in flight during this step's products.
+        if (nb > 0) load(0, kA, vA);
+        for (int j = 0; j < nb; j += 2) {
+            if (j + 1 < nb) load(j + 1, kB, vB);
+            compute(j, kA, vA);
+            if (j + 1 < nb) {
+                if (j + 2 < nb) load(j + 2, kA, vA);
+                compute(j + 1, kB, vB);
+            }
+        }
+        // Merge the waves: lane (l16, q4) holds head l16, columns 16cb + 4*q4 + v.
+        const float l = __shfl(lsum[0], l16);
+        if (q4 == 0) {
+            s_m[wave][l16] = nb > 0 ? m : -INFINITY;
+            s_l[wave][l16] = nb > 0 ? l : 0.f;
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s_o[wave][cb * 16 + 4 * q4 + v][l16] = nb > 0 ? o[cb][v] : 0.f;
+        __syncthreads();
+        const int64_t pbase = (((int64_t)b * a.G + g) * a.n_ch + ch) * a.R16 + h0;
+        for (int u = tid; u < 16 * D; u += kDecNW * 64) {
+            const int hh = u / D, c = u % D;
+            if (h0 + hh >= Rg) continue;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kDecNW; ++w) M = vmax(M, s_m[w][hh]);
+            float so = 0.f, sl = 0.f;
+#pragma unroll
+            for (int w = 0; w < kDecNW; ++w) {
+                const float f = s_m[w][hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[w][hh] - M);
+                so += f * s_o[w][c][hh];
+                sl += f * s_l[w][hh];
+            }
+            a.part_o[(pbase + hh) * D + c] = so;
+            if (c == 0) {
+                a.part_ml[(pbase + hh) * 2] = M;
+                a.part_ml[(pbase + hh) * 2 + 1] = sl;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Per sequence b: merges the chunks of every head (routed j = g*k + r, and
+// the shared head), normalises, and writes C[b] = [O_0 .. O_{Gk-1} |
+// sum_j w_j O_j | O_sh] in bf16 (the weighted slot from the bf16-rounded
+// hard slots, as the prefill forms it). One workgroup per sequence.
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* part_o, const float* part_ml,
+                                                             const int32_t* pos, const float* w, bf16* C, int G, int k,
+                                                             int s0, int d, int n_ch, int R16, int64_t ldc, int64_t T) {
+    const int b = blockIdx.x;
+    const int GK = G * k;
+    const int64_t p = pos[b];
+    // An out-of-range position reads no chunk (its slots are unspecified).
+    const int64_t len = (p < 0 || p >= T) ? 0 : p + 1;
+    const int nch = (int)min<int64_t>(n_ch, (len + kDecCH - 1) / kDecCH);
+    bf16* crow = C + (int64_t)b * ldc;
+    for (int u = threadIdx.x; u < (GK + 1) * d; u += blockDim.x) {
+        const int j = u / d, c = u % d;
+        const int g = j < GK ? j / k : s0, hd = j < GK ? j % k : k;   // the shared head is group s0's row k
+        const int64_t hb = (((int64_t)b * G + g) * n_ch) * R16 + hd;
+        float M = -INFINITY;
+        for (int i = 0; i < nch; ++i) M = fmaxf(M, part_ml[(hb + (int64_t)i * R16) * 2]);
+        float so = 0.f, sl = 0.f;
+        for (int i = 0; i < nch; ++i) {
+            const int64_t h = hb + (int64_t)i * R16;
+            const float f = __builtin_amdgcn_exp2f(part_ml[h * 2] - M);
+            so += f * part_o[h * d + c];
+            sl += f * part_ml[h * 2 + 1];
+        }
+        crow[(j < GK ? (int64_t)j : (int64_t)GK + 1) * d + c] = (bf16)(so / sl);
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+        float s = 0.f;
+        for (int j = 0; j < GK; ++j) s += w[(int64_t)b * GK + j] * (float)crow[(int64_t)j * d + c];
+        crow[(int64_t)GK * d + c] = (bf16)s;
+    }
+}
+
+}  // namespace gqe

@@ -24,6 +24,7 @@
 #include "attention.hpp"
 #include "attention_bwd.hpp"
 #include "backward.hpp"
+#include "decode.hpp"
 #include "gemm.hpp"
 #include "route.hpp"
 
@@ -322,7 +323,7 @@ struct TrainWs {
 };
 
 constexpr int kRowPad = kBwdDqBQ > 256 ? kBwdDqBQ : 256;   // row-space runs pad to whole dQ row tiles
-constexpr int kColsumRows = 1024;
+constexpr int kColsumRows = 256;
 
 // Splits of a weight-gradient GEMM over its token contraction: about 1024
 // workgroups (two rounds of MI355X's 256 CUs at two per CU), runs of at
@@ -542,7 +543,7 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
         ra.lg_col = (int)L.col_lg;
         ra.pad_col = (int)L.ccat;
         ra.coef = aux_coef;
-        hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, ra);
+        hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((N + 63) / 64)), dim3(64), 0, st, ra);
         hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)L.n_cs), dim3(256), 0, st, (const float*)F32(L.dz),
                            (const float*)F32(L.p), F32(L.cs), N, d.E, kColsumRows);
         hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(256), 0, st, (const float*)F32(L.cs), L.n_cs,
@@ -636,6 +637,116 @@ gqe_status fwd_impl(const gqe_shape* s, const void* x, const void* Wr, const flo
     if (idx_out && hipMemcpyAsync(idx_out, idx, picks * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return GQE_ERR_HIP;
     if (w_out && hipMemcpyAsync(w_out, w, picks * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return GQE_ERR_HIP;
     return GQE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one new token per sequence over a dense KV cache.
+// ---------------------------------------------------------------------------
+// The per-token part (projections, routing, permutation, sparse Q) runs as the
+// layer does on B tokens of length-1 sequences; the cache part has capacity T.
+gqe_status check_decode(const gqe_shape* s, Dims* cache, Dims* tok) {
+    gqe_status rc = check_shape(s, cache);
+    if (rc != GQE_OK) return rc;
+    if (cache->f32 || cache->variant != GQE_FULL) return GQE_ERR_UNSUPPORTED;
+    if (s->T % 32 != 0) return GQE_ERR_SHAPE;                // cache rows read in 32-key steps
+    gqe_shape t = *s;
+    t.T = 1;
+    return check_shape(&t, tok);
+}
+
+struct DecodeWs {
+    GqeWs tok;
+    size_t Kn, Vn, part_o, part_ml, total;
+    int n_ch, R16;
+};
+
+DecodeWs decode_layout(const Dims& c, const Dims& t) {
+    DecodeWs L;
+    L.tok = gqe_layout(t);
+    L.n_ch = (int)((c.T + kDecCH - 1) / kDecCH);
+    L.R16 = (int)align_up((size_t)(c.k + 1), 16);
+    size_t o = L.tok.total;
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+    L.Kn = take((size_t)t.N * c.G * c.d * 2);
+    L.Vn = take((size_t)t.N * c.G * c.d * 2);
+    const size_t heads = (size_t)c.B * c.G * L.n_ch * L.R16;
+    L.part_o = take(heads * c.d * 4);
+    L.part_ml = take(heads * 2 * 4);
+    L.total = o;
+    return L;
+}
+
+gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, const void* Wr, const float* br,
+                       const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo, void* k_cache,
+                       void* vt_cache, void* out, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                       void* stream, void* const* events) {
+    Dims c, t;
+    gqe_status rc = check_decode(s, &c, &t);
+    if (rc != GQE_OK) return rc;
+    if (!pos || !x || !Wr || !Wq || !Wk || !Wv || !Wq_sh || !Wo || !k_cache || !vt_cache || !out || !ws)
+        return GQE_ERR_NULL;
+    if (!aligned16(pos) || !aligned16(x) || !aligned16(Wr) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
+        !aligned16(Wq_sh) || !aligned16(Wo) || !aligned16(k_cache) || !aligned16(vt_cache) || !aligned16(out) ||
+        !aligned16(ws) || (br && !aligned16(br)) || (idx_out && !aligned16(idx_out)) || (w_out && !aligned16(w_out)))
+        return GQE_ERR_ALIGN;
+    const DecodeWs L = decode_layout(c, t);
+    if (ws_bytes < L.total) return GQE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const Marks mk{events, st};
+    const GqeWs& F = L.tok;
+    int32_t* idx = idx_out ? idx_out : (int32_t*)at(ws, F.idx);
+    float* w = w_out ? w_out : (float*)at(ws, F.w);
+    float* lg = (float*)at(ws, F.logits);
+    mk.at(0);
+    // New token: K, V rows, the shared head's query, router logits.
+    {
+        SegList sl = proj_base(t, x, t.D, t.N, (int)t.D);
+        sl.add(Wk, c.G * c.d, at(ws, L.Kn), OUT_ROWS, (int64_t)c.G * c.d, nullptr);
+        sl.add(Wq_sh, c.d, at(ws, F.Qsh), OUT_ROWS, c.d, nullptr, q_scale(c));
+        sl.add(Wr, c.E, lg, OUT_ROWS_F32, c.E, br);
+        sl.add(Wv, c.G * c.d, at(ws, L.Vn), OUT_ROWS, (int64_t)c.G * c.d, nullptr);
+        run_proj(t, sl, st);
+    }
+    hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)t.nC), dim3(256), 0, st, (const float*)lg, idx, w,
+                       (int32_t*)at(ws, F.hist), t.N, t.G, t.M, t.k, 1);
+    int32_t* cbase = (int32_t*)at(ws, F.cbase);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, (const int32_t*)at(ws, F.hist), cbase,
+                       (int32_t*)at(ws, F.offsets), (int32_t*)nullptr, (int)t.nC, t.E);
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)t.nC), dim3(256), 0, st, (const int32_t*)idx,
+                       (const int32_t*)cbase, (int32_t*)at(ws, F.perm), (int32_t*)at(ws, F.dst), t.N, t.G, t.M, t.k);
+    run_grouped_q(t, x, Wq, at(ws, F.Qr), (const int32_t*)at(ws, F.perm), (const int32_t*)at(ws, F.dst), cbase, st);
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)(c.B * c.G)), dim3(64), 0, st, (const bf16*)at(ws, L.Kn),
+                       (const bf16*)at(ws, L.Vn), pos, (bf16*)k_cache, (bf16*)vt_cache, c.T, (int)c.B, c.G, c.d);
+    mk.at(1);
+    DecodeArgs a;
+    a.Qr = (const bf16*)at(ws, F.Qr);
+    a.Qsh = (const bf16*)at(ws, F.Qsh);
+    a.K = (const bf16*)k_cache;
+    a.Vt = (const bf16*)vt_cache;
+    a.pos = pos;
+    a.part_o = (float*)at(ws, L.part_o);
+    a.part_ml = (float*)at(ws, L.part_ml);
+    a.T = c.T;
+    a.Bt = (int)c.B;
+    a.G = c.G;
+    a.k = c.k;
+    a.s0 = c.s0;
+    a.d = c.d;
+    a.n_ch = L.n_ch;
+    a.R16 = L.R16;
+    const dim3 grid((unsigned)((int64_t)c.B * c.G * L.n_ch));
+    if (c.d == 64) hipLaunchKernelGGL(attn_decode_kernel<64>, grid, dim3(kDecNW * 64), 0, st, a);
+    else hipLaunchKernelGGL(attn_decode_kernel<32>, grid, dim3(kDecNW * 64), 0, st, a);
+    mk.at(2);
+    bf16* C = (bf16*)at(ws, F.C);
+    const int64_t ldc = (int64_t)c.slots * c.d;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)c.B), dim3(256), 0, st, (const float*)a.part_o,
+                       (const float*)a.part_ml, pos, (const float*)w, C, c.G, c.k, c.s0, c.d, L.n_ch, L.R16, ldc, c.T);
+    SegList so = proj_base(t, C, ldc, t.N, (int)ldc);
+    so.add(Wo, (int)c.D, out, OUT_ROWS, c.D, nullptr);
+    run_proj(t, so, st);
+    mk.at(3);
+    return last_hip();
 }
 
 }  // namespace
@@ -735,6 +846,28 @@ gqe_status gqe_attn_bwd(const gqe_shape* s, const void* x, const void* Wr, const
                         float* aux_loss, void* ws, size_t ws_bytes, void* stream) {
     return bwd_impl(s, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, dx, dWr, dbr, dWq, dWk, dWv, dWq_sh, dWo,
                     aux_loss, ws, ws_bytes, stream, nullptr);
+}
+
+size_t gqe_decode_workspace_bytes(const gqe_shape* s) {
+    Dims c, t;
+    if (check_decode(s, &c, &t) != GQE_OK) return 0;
+    return decode_layout(c, t).total;
+}
+
+gqe_status gqe_decode_step(const gqe_shape* s, const int32_t* pos, const void* x, const void* Wr, const float* br,
+                           const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo,
+                           void* k_cache, void* vt_cache, void* out, int32_t* idx_out, float* w_out, void* ws,
+                           size_t ws_bytes, void* stream) {
+    return decode_impl(s, pos, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, k_cache, vt_cache, out, idx_out, w_out, ws, ws_bytes,
+                       stream, nullptr);
+}
+
+gqe_status gqe_decode_step_timed(const gqe_shape* s, const int32_t* pos, const void* x, const void* Wr,
+                                 const float* br, const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh,
+                                 const void* Wo, void* k_cache, void* vt_cache, void* out, int32_t* idx_out,
+                                 float* w_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+    return decode_impl(s, pos, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, k_cache, vt_cache, out, idx_out, w_out, ws, ws_bytes,
+                       stream, events);
 }
 
 // ---------------------------------------------------------------------------

@@ -165,3 +165,20 @@ def test_train_workspace_sizes(lib):
         prev = n
     s = shape(T=1 << 20, D=1024, G=8, M=2, d_h=64)
     assert lib.gqe_train_workspace_bytes(ctypes.byref(s)) < 64 << 30
+
+
+def test_decode_entry_point_validates(lib):
+    s = shape(T=256)
+    need = lib.gqe_decode_workspace_bytes(ctypes.byref(s))
+    assert need > 0
+    call = lambda sh, n, **o: lib.gqe_decode_step(
+        ctypes.byref(sh), o.get("pos", A), o.get("x", A), A, None, A, A, A, A, A, o.get("kc", A), A, o.get("out", A),
+        None, None, A, n, None)
+    assert call(s, need - 1) == -4
+    assert call(s, need, pos=None) == -1
+    assert call(s, need, kc=None) == -1
+    assert call(s, need, out=BAD) == -5
+    assert call(shape(T=250), 1 << 40) == -2                    # capacity not a multiple of 32
+    assert lib.gqe_decode_workspace_bytes(ctypes.byref(shape(T=250))) == 0
+    for kw in (dict(dtype=gq.GQE_F32), dict(variant=gq.GQE_NO_SHARED)):
+        assert call(shape(T=256, **kw), 1 << 40) == -3

@@ -1,0 +1,88 @@
+"""GPU parity of gqe_decode_step (one new token per sequence over a dense KV
+cache) against the fp64 decode oracle, through the C ABI.
+
+The caches hold seeded bf16 keys and values below each sequence's position
+and NaN from there on (positions past the cache length must never be read as
+data). Checked: the layer output on every sequence (the forward's bar,
+max|err| <= 1e-2 max|ref| + 1e-3), the routing (bit-exact), the appended key
+row and value column (bf16 of the oracle's projections, same bar), and that
+nothing else in either cache changed (bit-exact). Shapes: an empty prefix, a
+full cache, ragged positions, k = 2 with the shared head on group 1, and 17
+heads on one group (two passes of 16).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gqe_decode as gd
+import sparse_moe_attention_amd as gq
+from tests import harness as H
+from workloads import Shape, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+# (shape with T = cache capacity, positions)
+CASES = {
+    "ragged_k2_shared1": (Shape(B=3, T=256, D=128, G=3, M=3, k=2, d=32, router_bias=True, shared_kv_group=1),
+                          [0, 100, 255]),
+    "long_cache": (Shape(B=2, T=2048, D=256, G=8, M=2, k=1, d=64), [1500, 2047]),
+    "short": (Shape(B=4, T=64, D=64, G=2, M=2, k=1, d=64), [5, 0, 63, 31]),
+    "wide_pool": (Shape(B=2, T=1088, D=128, G=4, M=16, k=4, d=32, router_bias=True), [1087, 1024]),
+    "seventeen_heads": (Shape(B=2, T=320, D=64, G=2, M=20, k=16, d=32), [300, 17]),
+}
+
+
+def make_caches(s: Shape, pos, seed: int):
+    """bf16 caches in the library's layouts: keys [G][B][T][d], values
+    transposed [G][d][B*T]; N(0, 1) below pos[b], NaN from pos[b] on."""
+    gen = torch.Generator().manual_seed(seed)
+    k = torch.randn(s.G, s.B, s.T, s.d, generator=gen).to(torch.bfloat16)
+    v = torch.randn(s.G, s.B, s.T, s.d, generator=gen).to(torch.bfloat16)
+    for b, p in enumerate(pos):
+        k[:, b, p:] = float("nan")
+        v[:, b, p:] = float("nan")
+    vt = v.permute(0, 3, 1, 2).reshape(s.G, s.d, s.B * s.T).contiguous()
+    return k, v, vt
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_decode_parity(name):
+    s, pos = CASES[name]
+    print(f"[decode case {name}] {s} pos={pos}", flush=True)
+    inp = make_inputs(Shape(B=s.B, T=1, D=s.D, G=s.G, M=s.M, k=s.k, d=s.d, router_bias=s.router_bias,
+                            shared_kv_group=s.shared_kv_group), seed=500 + len(name))
+    kc, vc, vtc = make_caches(s, pos, seed=600 + len(name))
+    dv = H.to_device(inp)
+    kd, vtd = kc.cuda(), vtc.cuda()
+    posd = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    sh = gq.shape_from(s)
+    ws = torch.empty(gq.gqe_decode_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    out = torch.empty(s.B, s.D, dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(s.B, s.G, s.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(s.B, s.G, s.k, dtype=torch.float32, device="cuda")
+    gq.gqe_decode_step(sh, posd, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"], dv["Wo"],
+                       kd, vtd, out, ws, idx, w)
+    torch.cuda.synchronize()
+
+    f = H.f64_inputs(inp)
+    k64 = kc.float().numpy().astype(np.float64).transpose(1, 0, 2, 3)       # [B, G, T, d]
+    v64 = vc.float().numpy().astype(np.float64).transpose(1, 0, 2, 3)
+    ref = gd.gqe_decode(f, k64, v64, pos, s.G, s.M, s.k, s.d, shared_kv_group=s.shared_kv_group)
+    assert (idx.cpu().numpy() == ref["idx"]).all(), (name, "routing")
+    err, bound = H.out_error(H.np32(out), ref["out"])
+    assert np.isfinite(H.np32(out)).all() and err <= bound, (name, "out", err, bound)
+
+    # the appended row / column, and nothing else changed
+    k_after = kd.cpu()
+    v_after = vtd.cpu().reshape(s.G, s.d, s.B, s.T).permute(0, 2, 3, 1)    # [G, B, T, d]
+    for b, p in enumerate(pos):
+        err, bound = H.out_error(k_after[:, b, p].float().numpy(), ref["K_new"][b])
+        assert err <= bound, (name, "appended key", b, err, bound)
+        err, bound = H.out_error(v_after[:, b, p].float().numpy(), ref["V_new"][b])
+        assert err <= bound, (name, "appended value", b, err, bound)
+        k_after[:, b, p] = kc[:, b, p]
+        v_after[:, b, p] = vc[:, b, p]
+    assert torch.equal(k_after.view(torch.int16), kc.view(torch.int16)), (name, "key cache changed elsewhere")
+    assert torch.equal(v_after.contiguous().view(torch.int16), vc.view(torch.int16)), (name, "value cache changed")
