@@ -10,7 +10,9 @@ k=1, d_h=64, bf16). Prints ONE JSON line with tokens/s, the attention kernel's
 MFMA roofline fraction (timed live with HIP events on the library's stream),
 the speedup over dense 16q/8kv GQA built from the same kernels, the training
 step (forward that keeps its state + backward, with the attention backward's
-MFMA rate), and the fp64 oracle timed on the host's cores (a baseline only).
+MFMA rate), a decode step (16 sequences over a dense KV cache of the
+workload's length, with the cache read's HBM rate), and the fp64 oracle timed
+on the host's cores (a baseline only).
 """
 from __future__ import annotations
 
@@ -110,6 +112,58 @@ def train_leg(gq, torch, s, dv, steps, warmup, mk_events):
             "aux_coef": coef}
 
 
+DECODE_B = 16
+
+
+def decode_leg(gq, torch, s, dv, steps, warmup, mk_events):
+    """One decode step per sequence over a dense KV cache: B = 16 sequences
+    with T - 1 cached positions each (the new token at T - 1), the layer of
+    the workload otherwise. Synthetic bf16 caches. Returns the record's
+    "decode_step" object with the attention-over-cache kernel's HBM rate."""
+    import dataclasses
+    from workloads import Shape, make_inputs
+    B, T = DECODE_B, s.T
+    ds = Shape(B=B, T=T, D=s.D, G=s.G, M=s.M, k=s.k, d=s.d, router_bias=s.router_bias,
+               shared_kv_group=s.shared_kv_group)
+    tok = make_inputs(dataclasses.replace(ds, T=1), seed=4000)
+    w = {k: (v.cuda() if v is not None else None) for k, v in tok.items()}
+    gen = torch.Generator(device="cuda").manual_seed(4001)
+    kc = torch.randn(ds.G, B, T, ds.d, device="cuda", generator=gen).to(torch.bfloat16)
+    vtc = torch.randn(ds.G, ds.d, B * T, device="cuda", generator=gen).to(torch.bfloat16)
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    sh = gq.shape_from(ds)
+    ws = torch.empty(gq.gqe_decode_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, ds.D, dtype=torch.bfloat16, device="cuda")
+
+    def step(ev=None):
+        gq.gqe_decode_step(sh, pos, w["x"], w["Wr"], w["br"], w["Wq"], w["Wk"], w["Wv"], w["Wq_sh"], w["Wo"], kc,
+                           vtc, out, ws, events=ev)
+
+    for _ in range(warmup):
+        step()
+    n = max(steps, 20)
+    ev = [mk_events(gq.GQE_DECODE_N_STAGES + 1) for _ in range(n)]
+    t0, t1 = mk_events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for e in ev:
+        step(gq.event_array(e))
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n
+    stage = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / n for i in range(gq.GQE_DECODE_N_STAGES)]
+    attn_ms = stage[1]
+    kv_bytes = 2.0 * B * ds.G * T * ds.d * 2          # every cached key and value read once
+    gbs = kv_bytes / (attn_ms * 1e-3) / 1e9
+    return {"tokens_per_s": B / (ms / 1e3), "ms_per_step": ms,
+            "workload": f"{B} sequences x {T - 1} cached positions, one new token each, D{ds.D} G{ds.G} "
+                        f"M{ds.M} k{ds.k} d{ds.d} bf16",
+            "stage_ms": {nm: round(v, 4) for nm, v in zip(gq.GQE_DECODE_STAGE_NAMES, stage)},
+            "attn_roofline": {"bound": "hbm", "kernel": "attn_decode_kernel", "achieved": gbs, "peak": 8000.0,
+                              "unit": "GB/s", "frac": gbs / 8000.0, "algorithmic_bytes_per_launch": kv_bytes,
+                              "avg_launch_ms": attn_ms}}
+
+
 def source_sha(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -180,6 +234,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gqa", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the training-step (forward + backward) leg")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--variant", default="full", choices=["full", "weighted_concat", "hard_concat", "no_shared"],
                     help="merge of the picked experts: the layer, or one of the pages' ablations")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -291,6 +346,10 @@ def main():
     if not args.no_backward and s.dtype == "bf16" and s.variant == "full":
         bwd = train_leg(gq, torch, s, dv, steps, args.warmup, mk_events)
 
+    dec = None
+    if not args.no_decode and s.dtype == "bf16" and s.variant == "full" and s.T % 32 == 0:
+        dec = decode_leg(gq, torch, s, dv, steps, args.warmup, mk_events)
+
     peak = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
     fl = attn_flops(s, active_heads(s))
     achieved = fl / (attn_ms / 1e3) / 1e12
@@ -318,6 +377,7 @@ def main():
         "stage_ms": stage_ms,
         "gqa_baseline": gqa,
         "training_step": bwd,
+        "decode_step": dec,
         "wall_s_timed_region": wall,
         "cpu_baseline": None,
     }

@@ -11,8 +11,9 @@
 //     O^T = V^T P^T) for all query heads of the group at once (the picked
 //     experts and, on its group, the shared head, zero-padded to 16), with an
 //     online softmax, and writes the chunk's (max, sum, unnormalised output);
-//   * decode_combine_kernel: merges the chunks of every head, then writes the
-//     merged slots C = [hard | weighted | shared] for the output projection.
+//   * decode_combine_kernel: merges the chunks of every head into its slot of
+//     C = [hard | weighted | shared] (the weighted slot is then formed by the
+//     prefill's combine kernel) for the output projection.
 // The cache layout is the prefill's: keys [G][B][T][d] (one contiguous row
 // per key), values transposed [G][d][B*T] (contiguous keys per column).
 #pragma once
@@ -201,41 +202,32 @@ __global__ __launch_bounds__(kDecNW * 64) void attn_decode_kernel(DecodeArgs a) 
     }
 }
 
-// Per sequence b: merges the chunks of every head (routed j = g*k + r, and
-// the shared head), normalises, and writes C[b] = [O_0 .. O_{Gk-1} |
-// sum_j w_j O_j | O_sh] in bf16 (the weighted slot from the bf16-rounded
-// hard slots, as the prefill forms it). One workgroup per sequence.
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float* part_o, const float* part_ml,
-                                                             const int32_t* pos, const float* w, bf16* C, int G, int k,
-                                                             int s0, int d, int n_ch, int R16, int64_t ldc, int64_t T) {
-    const int b = blockIdx.x;
+// Merges the chunks of one head of one sequence (workgroup (b, j): routed
+// head j = g*k + r, or j = G*k for the shared head) and writes its slot of
+// C[b] = [O_0 .. O_{Gk-1} | weighted | O_sh] in bf16. The weighted slot is
+// formed afterwards from the bf16 hard slots, as in the prefill.
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* part_o, const float* part_ml,
+                                                            const int32_t* pos, bf16* C, int G, int k, int s0, int d,
+                                                            int n_ch, int R16, int64_t ldc, int64_t T) {
     const int GK = G * k;
+    const int b = blockIdx.x / (GK + 1), j = blockIdx.x % (GK + 1), c = threadIdx.x;
+    if (c >= d) return;
     const int64_t p = pos[b];
     // An out-of-range position reads no chunk (its slots are unspecified).
     const int64_t len = (p < 0 || p >= T) ? 0 : p + 1;
     const int nch = (int)min<int64_t>(n_ch, (len + kDecCH - 1) / kDecCH);
-    bf16* crow = C + (int64_t)b * ldc;
-    for (int u = threadIdx.x; u < (GK + 1) * d; u += blockDim.x) {
-        const int j = u / d, c = u % d;
-        const int g = j < GK ? j / k : s0, hd = j < GK ? j % k : k;   // the shared head is group s0's row k
-        const int64_t hb = (((int64_t)b * G + g) * n_ch) * R16 + hd;
-        float M = -INFINITY;
-        for (int i = 0; i < nch; ++i) M = fmaxf(M, part_ml[(hb + (int64_t)i * R16) * 2]);
-        float so = 0.f, sl = 0.f;
-        for (int i = 0; i < nch; ++i) {
-            const int64_t h = hb + (int64_t)i * R16;
-            const float f = __builtin_amdgcn_exp2f(part_ml[h * 2] - M);
-            so += f * part_o[h * d + c];
-            sl += f * part_ml[h * 2 + 1];
-        }
-        crow[(j < GK ? (int64_t)j : (int64_t)GK + 1) * d + c] = (bf16)(so / sl);
+    const int g = j < GK ? j / k : s0, hd = j < GK ? j % k : k;   // the shared head is group s0's row k
+    const int64_t hb = (((int64_t)b * G + g) * n_ch) * R16 + hd;
+    float M = -INFINITY;
+    for (int i = 0; i < nch; ++i) M = fmaxf(M, part_ml[(hb + (int64_t)i * R16) * 2]);
+    float so = 0.f, sl = 0.f;
+    for (int i = 0; i < nch; ++i) {
+        const int64_t h = hb + (int64_t)i * R16;
+        const float f = __builtin_amdgcn_exp2f(part_ml[h * 2] - M);
+        so += f * part_o[h * d + c];
+        sl += f * part_ml[h * 2 + 1];
     }
-    __syncthreads();
-    for (int c = threadIdx.x; c < d; c += blockDim.x) {
-        float s = 0.f;
-        for (int j = 0; j < GK; ++j) s += w[(int64_t)b * GK + j] * (float)crow[(int64_t)j * d + c];
-        crow[(int64_t)GK * d + c] = (bf16)s;
-    }
+    C[(int64_t)b * ldc + (j < GK ? (int64_t)j : (int64_t)GK + 1) * d + c] = (bf16)(so / sl);
 }
 
 }  // namespace gqe
