@@ -33,6 +33,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (fp32 layers run fp32 MFMA)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "sparse_moe_attention_amd", "csrc", "attention.hpp")
+DECODE_SRC = os.path.join(ROOT, "sparse_moe_attention_amd", "csrc", "decode.hpp")
 
 
 def attn_flops(s, heads: int) -> float:
@@ -115,7 +116,7 @@ def train_leg(gq, torch, s, dv, steps, warmup, mk_events):
 DECODE_B = 16
 
 
-def decode_leg(gq, torch, s, dv, steps, warmup, mk_events):
+def decode_leg(gq, torch, s, dv, steps, warmup, mk_events, cid):
     """One decode step per sequence over a dense KV cache: B = 16 sequences
     with T - 1 cached positions each (the new token at T - 1), the layer of
     the workload otherwise. Synthetic bf16 caches. Returns the record's
@@ -160,8 +161,9 @@ def decode_leg(gq, torch, s, dv, steps, warmup, mk_events):
                         f"M{ds.M} k{ds.k} d{ds.d} bf16",
             "stage_ms": {nm: round(v, 4) for nm, v in zip(gq.GQE_DECODE_STAGE_NAMES, stage)},
             "attn_roofline": {"bound": "hbm", "kernel": "attn_decode_kernel", "achieved": gbs, "peak": 8000.0,
-                              "unit": "GB/s", "frac": gbs / 8000.0, "algorithmic_bytes_per_launch": kv_bytes,
-                              "avg_launch_ms": attn_ms}}
+                              "unit": "GB/s", "frac": gbs / 8000.0,
+                              "traffic": measured_traffic(f"decode_config{cid}", DECODE_SRC),
+                              "algorithmic_bytes_per_launch": kv_bytes, "avg_launch_ms": attn_ms}}
 
 
 def source_sha(path: str) -> str:
@@ -169,16 +171,16 @@ def source_sha(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(config_id: int):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+def measured_traffic(key: str, src: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (entry `key`), if it was taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = t.get(f"config{config_id}")
-    if not entry or entry.get("attention_src_sha") != source_sha(ATTN_SRC):
+    entry = t.get(key)
+    if not entry or entry.get("src_sha") != source_sha(src):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -348,12 +350,12 @@ def main():
 
     dec = None
     if not args.no_decode and s.dtype == "bf16" and s.variant == "full" and s.T % 32 == 0:
-        dec = decode_leg(gq, torch, s, dv, steps, args.warmup, mk_events)
+        dec = decode_leg(gq, torch, s, dv, steps, args.warmup, mk_events, args.config)
 
     peak = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
     fl = attn_flops(s, active_heads(s))
     achieved = fl / (attn_ms / 1e3) / 1e12
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(f"config{args.config}", ATTN_SRC)
     rec = {
         "metric": METRIC,
         "value": s.N / (ms_step / 1e3),

@@ -49,12 +49,19 @@ struct DecodeArgs {
     int32_t R16;          // head slots per group, a multiple of 16 (>= k + 1)
 };
 
+#ifndef GQE_DEC_CW
+#define GQE_DEC_CW 512
+#endif
+#ifndef GQE_DEC_WPE
+#define GQE_DEC_WPE 2
+#endif
 constexpr int kDecNW = 4;          // waves per workgroup
-constexpr int kDecCW = 256;        // keys per wave
+constexpr int kDecCW = GQE_DEC_CW; // keys per wave
 constexpr int kDecCH = kDecNW * kDecCW;
 
 template <int D>
-__global__ __launch_bounds__(kDecNW * 64) void attn_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(GQE_DEC_WPE)))
+void attn_decode_kernel(DecodeArgs a) {
     constexpr int DK = D / 32, CB = D / 16;
     constexpr int NB = kDecCW / 32;                 // 32-key steps per wave
     const int tid = threadIdx.x, lane = tid & 63;
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(kDecNW * 64) void attn_decode_kernel(DecodeArgs a) 
             for (int cb = 0; cb < CB; ++cb) vf[cb] = ld_frag<bf16>(Vg + (int64_t)(cb * 16 + l16) * vrow + k0 + 8 * q4);
         };
         Frag<bf16> kA[2][DK], vA[CB], kB[2][DK], vB[CB];
-        auto compute = [&](int j, const Frag<bf16> (&kf)[2][DK], const Frag<bf16> (&vfin)[CB]) {
+        auto compute = [&](int j, const Frag<bf16> (&kf)[2][DK], Frag<bf16> (&vf)[CB]) {
             const int64_t k0 = w0 + 32 * j;
             f32x4 s[2];
 #pragma unroll
@@ -117,9 +124,6 @@ __global__ __launch_bounds__(kDecNW * 64) void attn_decode_kernel(DecodeArgs a) 
 #pragma unroll
                 for (int dk = 0; dk < DK; ++dk) s[kb] = mma16(kf[kb][dk], qf[dk], s[kb]);
             }
-            Frag<bf16> vf[CB];
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) vf[cb] = vfin[cb];
             if (k0 + 32 > len) {
                 // Keys at or past len are not attended: their scores become -inf
                 // and their values 0 (the cache there may hold any bits, and a
