@@ -85,8 +85,11 @@ struct AttnBwdArgs {
 #define GQE_BWD_DQ_WPE 2
 #endif
 constexpr int kBwdKW = GQE_BWD_KW;         // keys per wave (dK/dV kernel)
-constexpr int kBwdNW = GQE_BWD_NW;         // waves per dK/dV workgroup
-constexpr int kBwdBK = kBwdKW * kBwdNW;    // keys per dK/dV workgroup
+// Waves per dK/dV workgroup: head width 32 stages half the bytes per step,
+// which 512 threads do not split evenly, so it keeps 4 waves.
+template <int D> constexpr int bwd_nw() { return D == 64 ? GQE_BWD_NW : 4; }
+template <int D> constexpr int bwd_bk() { return kBwdKW * bwd_nw<D>(); }   // keys per dK/dV workgroup
+constexpr int kBwdBKMax = kBwdKW * (GQE_BWD_NW > 4 ? GQE_BWD_NW : 4);
 constexpr int kBwdQB = 64;                 // query rows per staged step (dK/dV kernel)
 constexpr int kBwdRS = GQE_BWD_RS;         // rows per sub-step
 constexpr int kBwdDqQW = GQE_BWD_DQ_QW;    // rows per wave (dQ kernel)
@@ -103,9 +106,10 @@ static_assert(kBwdDqQW % 16 == 0 && kBwdBKV % kBwdDqKS == 0 && kBwdDqKS % 32 == 
 __device__ __forceinline__ int qrow_of(int qb, int i) { return key_of_row(qb, i); }
 
 template <int D>
-__global__ __launch_bounds__(kBwdNW * 64) __attribute__((amdgpu_waves_per_eu(GQE_BWD_WPE, GQE_BWD_WPE)))
+__global__ __launch_bounds__(bwd_nw<D>() * 64) __attribute__((amdgpu_waves_per_eu(GQE_BWD_WPE, GQE_BWD_WPE)))
 void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
-    constexpr int NT = kBwdNW * 64;
+    constexpr int NT = bwd_nw<D>() * 64;
+    constexpr int kBwdBK = bwd_bk<D>();
     constexpr int KB = kBwdKW / 16;            // 16-key blocks per wave
     constexpr int DK = D / 32;                 // contraction steps over d
     constexpr int CB = D / 16;                 // 16-row blocks of dK^T / dV^T
@@ -219,11 +223,16 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
             nls[qq] = *reinterpret_cast<const f32x4*>(aux + 16 * chunk);
             ndl[qq] = *reinterpret_cast<const f32x4*>(aux + 256 + 16 * chunk);
         }
-        // Contraction steps outermost: dependent products stay QBS*KB*2 apart.
+        // Score products 32 rows at a time (contraction steps inner for each
+        // half): the exponent work of the first half can then overlap the
+        // second half's products, and its dV/dK products the second half's
+        // exponents.
+#pragma unroll
+        for (int hh = 0; hh < QBS / 2; ++hh)
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
-            for (int qq = 0; qq < QBS; ++qq) {
+            for (int qq = 2 * hh; qq < 2 * hh + 2; ++qq) {
                 const int qr = qrow_of(QBS * h + qq, l16), c = 4 * dk + q4;
                 const Frag<bf16> qf = ld_frag<bf16>(Qs + k_chunk_off<QCH>(qr, c));
                 const Frag<bf16> of = ld_frag<bf16>(dOs + k_chunk_off<QCH>(qr, c));
@@ -245,21 +254,21 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
                         if (qrow_of(QBS * h + qq, 4 * q4 + v) < lim) s[qq][kb][v] = -INFINITY;
             }
         }
-#pragma unroll
-        for (int qq = 0; qq < QBS; ++qq)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float pv = __builtin_amdgcn_exp2f(s[qq][kb][v]);
-                    s[qq][kb][v] = pv;
-                    dp[qq][kb][v] = pv * dp[qq][kb][v];
-                }
         // P and dS fragments, 32 rows per contraction step: lane group q4
         // holds rows 32j + 8*q4 .. +7 of key column l16.
 #pragma unroll
         for (int jj = 0; jj < QBS / 2; ++jj) {
             const int j32 = (QBS / 2) * h + jj;              // 32-row step within the 64 rows
+#pragma unroll
+            for (int qq = 2 * jj; qq < 2 * jj + 2; ++qq)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float pv = __builtin_amdgcn_exp2f(s[qq][kb][v]);
+                        s[qq][kb][v] = pv;
+                        dp[qq][kb][v] = pv * dp[qq][kb][v];
+                    }
             Frag<bf16> pf[KB], sf[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)

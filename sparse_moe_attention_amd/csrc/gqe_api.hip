@@ -43,7 +43,9 @@ using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
 
 constexpr int kAttnWaves = kAttnNW;             // waves per attention workgroup
 constexpr int kBQ = kAttnWaves * kAttnQW;       // attention query tile
-constexpr int kKVPad = kAttnBKV;  // sequence padding of the K / V^T buffers: whole key tiles
+// Sequence padding of the K / V^T buffers: whole key tiles of the forward
+// and whole key blocks of the dK/dV kernel (its waves read their keys' rows).
+constexpr int kKVPad = kAttnBKV > kBwdBKMax ? kAttnBKV : kBwdBKMax;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -564,10 +566,11 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
     ab.G = d.G; ab.M = d.M; ab.k = d.k;
     ab.colK = (int)L.col_k; ab.colV = (int)L.col_v; ab.colQsh = (int)L.col_qsh;
     {
-        ab.n_tiles = (int)((d.T + kBwdBK - 1) / kBwdBK);
+        const int bk = d.d == 64 ? bwd_bk<64>() : bwd_bk<32>();
+        ab.n_tiles = (int)((d.T + bk - 1) / bk);
         const dim3 grid((unsigned)((int64_t)ab.n_tiles * d.G * d.B));
-        if (d.d == 64) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, dim3(kBwdNW * 64), 0, st, ab);
-        else hipLaunchKernelGGL(attn_bwd_dkdv_kernel<32>, grid, dim3(kBwdNW * 64), 0, st, ab);
+        if (d.d == 64) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, dim3(bwd_nw<64>() * 64), 0, st, ab);
+        else hipLaunchKernelGGL(attn_bwd_dkdv_kernel<32>, grid, dim3(bwd_nw<32>() * 64), 0, st, ab);
     }
     mk.at(4);
     {
