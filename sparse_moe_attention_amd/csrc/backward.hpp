@@ -218,8 +218,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 //   dz[g,m] = p[g,m] * (dp[g,m] - sum_m' p[g,m'] dp[g,m']).
 // Writes dz in fp32 (for the bias gradient) and bf16 into the gradient
 // matrix dY at column lg_col, p in fp32 (for the balancing loss), and zeros
-// into dY's d columns of every expert the token did not pick and into the
-// padding columns [pad_col, ldy).
+// into the padding columns [pad_col, ldy). (The d columns of the experts a
+// token did not pick are zeroed by zero_cols_kernel.)
 // ---------------------------------------------------------------------------
 struct RouterBwdArgs {
     const float* logits;     // [N, E]
@@ -256,7 +256,6 @@ __global__ __launch_bounds__(64) void router_bwd_kernel(RouterBwdArgs a) {
         }
     }
     const float aux = a.coef * (float)a.M / ((float)a.G * (float)a.N * (float)a.N * (float)a.k);
-    const bf16x8 z8 = {};
     for (int g = 0; g < a.G; ++g) {
         float mx = -INFINITY;
         for (int m = 0; m < a.M; ++m) mx = fmaxf(mx, lg[g * a.M + m]);
@@ -287,8 +286,6 @@ __global__ __launch_bounds__(64) void router_bwd_kernel(RouterBwdArgs a) {
             a.dz[n * E + e] = dz;
             a.p[n * E + e] = pm;
             dy[a.lg_col + e] = (bf16)dz;
-            if (!pk)
-                for (int c = 0; c < a.d; c += 8) *reinterpret_cast<bf16x8*>(dy + (int64_t)e * a.d + c) = z8;
         }
     }
     for (int c = a.pad_col; c < a.ldy; ++c) dy[c] = (bf16)0.f;
@@ -323,27 +320,46 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* a, const float
 }
 
 // dbr[e] = sum of the dz partials; the balancing loss
-// coef/G * sum_{g,m} M * f[g,m] * mean_n p[n,g,m].
+// coef/G * sum_{g,m} M * f[g,m] * mean_n p[n,g,m]. The L = 256 / E lanes of
+// expert e take partials i = lane, lane + L, ...; their sums are then added
+// in lane order (deterministic).
 __global__ __launch_bounds__(256) void finalize_kernel(const float* part, int nblk, const int32_t* offsets, int64_t N,
                                                        int G, int M, int k, float coef, float* dbr, float* aux_loss) {
-    __shared__ float term[256];
-    const int E = G * M;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        float sz = 0.f, sp = 0.f;
-        for (int i = 0; i < nblk; ++i) {
+    __shared__ float rz[256], rp[256], term[256];
+    const int E = G * M, L = 256 / E, tid = threadIdx.x, e = tid % E, lane = tid / E;
+    float sz = 0.f, sp = 0.f;
+    if (lane < L)
+        for (int i = lane; i < nblk; i += L) {
             sz += part[(int64_t)i * E + e];
             sp += part[(int64_t)(nblk + i) * E + e];
         }
-        if (dbr != nullptr) dbr[e] = sz;
-        const float f = (float)(offsets[e + 1] - offsets[e]) / ((float)N * (float)k);
-        term[e] = (float)M * f * (sp / (float)N);
+    rz[tid] = sz;
+    rp[tid] = sp;
+    __syncthreads();
+    if (tid < E) {
+        float z = 0.f, q = 0.f;
+        for (int l = 0; l < L; ++l) {
+            z += rz[l * E + tid];
+            q += rp[l * E + tid];
+        }
+        if (dbr != nullptr) dbr[tid] = z;
+        const float f = (float)(offsets[tid + 1] - offsets[tid]) / ((float)N * (float)k);
+        term[tid] = (float)M * f * (q / (float)N);
     }
     __syncthreads();
-    if (threadIdx.x == 0 && aux_loss != nullptr) {
+    if (tid == 0 && aux_loss != nullptr) {
         float s = 0.f;
-        for (int e = 0; e < E; ++e) s += term[e];
+        for (int i = 0; i < E; ++i) s += term[i];
         *aux_loss = coef * s / (float)G;
     }
+}
+
+// Zeroes columns [0, cols) of every row of a bf16 matrix (row stride ld,
+// both multiples of 8): 16 bytes per thread, consecutive threads along a row.
+__global__ __launch_bounds__(256) void zero_cols_kernel(bf16* m, int64_t rows, int64_t cols, int64_t ld) {
+    const int64_t per = cols / 8, q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= rows * per) return;
+    *reinterpret_cast<bf16x8*>(m + (q / per) * ld + (q % per) * 8) = bf16x8{};
 }
 
 // ---------------------------------------------------------------------------

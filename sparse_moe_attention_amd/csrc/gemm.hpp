@@ -375,8 +375,9 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* l
         if (a.seg[s].col_begin <= n0 && n0 + Cfg::BN <= a.seg[s].col_begin + a.seg[s].n_cols) full_seg = s;
     const bool fast = full_seg >= 0 && m0 + Cfg::BM <= a.M_rows && t0 + Cfg::BM <= a.T && (t0 & 3) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.seg[full_seg].out) & 15) == 0 &&
-                      (a.seg[full_seg].mode != OUT_ROWS || (a.seg[full_seg].ld_out & 3) == 0) &&
-                      a.seg[full_seg].mode != OUT_ROWS_F32;
+                      (a.seg[full_seg].mode == OUT_HEADS || a.seg[full_seg].mode == OUT_HEADS_T ||
+                       (a.seg[full_seg].ld_out & 3) == 0) &&
+                      (a.seg[full_seg].mode != OUT_ROWS_F32 || a.seg[full_seg].bias == nullptr);
 
     if (trans) {
         // Transposed heads: a lane holds tokens r .. r+3 of column c.
@@ -438,6 +439,16 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* l
             for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < Cfg::FN; ++j) store4<T>(p + (int64_t)i * 16 * sg.ld_out + j * 16, acc[i][j], sg.scale);
+        } else if (sg.mode == OUT_ROWS_F32) {   // no bias (checked above); split-K partial at offset so
+            float* p = (float*)sg.out + so + (m0 + r0) * sg.ld_out + c0;
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j) {
+                    float* o = p + (int64_t)i * 16 * sg.ld_out + j * 16;
+                    if (ns > 1) *reinterpret_cast<f32x4*>(o) = acc[i][j] * sg.scale;   // read back at once: keep in L2
+                    else store4<float>(o, acc[i][j], sg.scale);
+                }
         } else {   // OUT_HEADS: token rows of one sequence, d-wide head rows
             const int64_t hstride = (int64_t)a.Bt * a.Tpad * a.d;
             T* p = (T*)sg.out + (b0 * a.Tpad + t0 + r0) * a.d;

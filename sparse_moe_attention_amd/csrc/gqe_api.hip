@@ -545,6 +545,10 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
         ra.lg_col = (int)L.col_lg;
         ra.pad_col = (int)L.ccat;
         ra.coef = aux_coef;
+        // dQ columns of every expert start at zero; the dQ kernel writes the picked ones.
+        const int64_t zq = N * ((int64_t)d.E * d.d / 8);
+        hipLaunchKernelGGL(zero_cols_kernel, dim3((unsigned)((zq + 255) / 256)), dim3(256), 0, st, B(L.dY), N,
+                           (int64_t)d.E * d.d, L.ccat_pad);
         hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((N + 63) / 64)), dim3(64), 0, st, ra);
         hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)L.n_cs), dim3(256), 0, st, (const float*)F32(L.dz),
                            (const float*)F32(L.p), F32(L.cs), N, d.E, kColsumRows);
