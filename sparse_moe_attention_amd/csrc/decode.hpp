@@ -4,7 +4,9 @@
 // Experts" explainer, technical summary, "Architecture and routing";
 // FrontiersMind GQE article, part 4). Reading the cache dominates, so the
 // attention kernel is an HBM stream:
-//   * append_kernel: the new token's key row and value column into the cache;
+//   * decode_token_kernel: per (sequence, group), the group's routing, the
+//     picked experts' queries, and the new key row and value column appended
+//     to the cache;
 //   * attn_decode_kernel: one workgroup per (sequence, group, chunk of cached
 //     keys); each wave streams its keys straight from HBM into MFMA operands
 //     (K rows as the A operand of S^T = K Q^T, V^T rows as the A operand of
@@ -19,20 +21,74 @@
 #pragma once
 
 #include "attention.hpp"
+#include "route.hpp"
 
 namespace gqe {
 
-// k_cache[g][b][pos[b]] = Kn[b][g], vt_cache[g][c][b*T + pos[b]] = Vn[b][g][c].
-// Grid B*G, 64 threads (d <= 64).
-__global__ __launch_bounds__(64) void append_kernel(const bf16* Kn, const bf16* Vn, const int32_t* pos, bf16* kc,
-                                                    bf16* vtc, int64_t T, int Bt, int G, int d) {
-    const int b = blockIdx.x / G, g = blockIdx.x % G, c = threadIdx.x;
-    if (c >= d) return;
-    const int64_t p = pos[b];
-    if (p < 0 || p >= T) return;    // refused on the host when it can be checked; never written
-    const int64_t src = ((int64_t)b * G + g) * d + c;
-    kc[(((int64_t)g * Bt + b) * T + p) * d + c] = Kn[src];
-    vtc[((int64_t)g * d + c) * ((int64_t)Bt * T) + (int64_t)b * T + p] = Vn[src];
+// Token side of one (sequence b, group g), one workgroup each: the group's
+// top-k from the router logits (as route_kernel picks them), the queries of
+// the picked experts Qr[b][g*k + r] = x[b] Wq_e^T (pre-scaled), and the new
+// key row and value column appended to the cache at pos[b]. Workgroup
+// (b, 0) also writes the token's full routing (idx, renormalised w).
+// 256 threads: 256 / d lanes per output column, each a strided share of D.
+struct DecTokArgs {
+    const float* logits;  // [B, G*M]
+    const bf16* x;        // [B, D]
+    const bf16* Wq;       // [G*M*d, D]
+    const bf16* Kn;       // [B, G*d] the new keys
+    const bf16* Vn;       //          and values
+    const int32_t* pos;
+    int32_t* idx;         // [B, G*k]
+    float* w;
+    bf16* Qr;             // [B, G*k, d]
+    bf16* kc;             // [G][B][T][d]
+    bf16* vtc;            // [G][d][B*T]
+    int64_t T, D;
+    int32_t Bt, G, M, k, d;
+    float qscale;
+};
+
+__global__ __launch_bounds__(256) void decode_token_kernel(DecTokArgs a) {
+    __shared__ int32_t s_sel[64];
+    __shared__ float s_prob[64];
+    const int b = blockIdx.x / a.G, g = blockIdx.x % a.G, tid = threadIdx.x;
+    const float* z = a.logits + (int64_t)b * a.G * a.M;
+    if (tid == 0) {
+        topk_group(z + g * a.M, a.M, a.k, s_sel, s_prob);
+        if (g == 0) {   // the whole token's routing: the same picks and weights as route_kernel
+            int32_t* irow = a.idx + (int64_t)b * a.G * a.k;
+            float* wrow = a.w + (int64_t)b * a.G * a.k;
+            float total = 0.f;
+            for (int gg = 0; gg < a.G; ++gg) {
+                topk_group(z + gg * a.M, a.M, a.k, irow + gg * a.k, wrow + gg * a.k);
+                for (int r = 0; r < a.k; ++r) total += wrow[gg * a.k + r];
+            }
+            const float inv = 1.f / total;
+            for (int q = 0; q < a.G * a.k; ++q) wrow[q] = wrow[q] * inv;
+        }
+    }
+    const int64_t p = a.pos[b];
+    if (tid < a.d && p >= 0 && p < a.T) {
+        const int64_t src = ((int64_t)b * a.G + g) * a.d + tid;
+        a.kc[(((int64_t)g * a.Bt + b) * a.T + p) * a.d + tid] = a.Kn[src];
+        a.vtc[((int64_t)g * a.d + tid) * ((int64_t)a.Bt * a.T) + (int64_t)b * a.T + p] = a.Vn[src];
+    }
+    __syncthreads();
+    const int tpo = 256 / a.d, c = tid / tpo, part = tid % tpo;   // tpo lanes per output column
+    const bf16* xr = a.x + (int64_t)b * a.D;
+    for (int r = 0; r < a.k; ++r) {
+        const bf16* wr = a.Wq + ((int64_t)(g * a.M + s_sel[r]) * a.d + c) * a.D;
+        float acc = 0.f;
+        for (int64_t i = 8 * part; i < a.D; i += 8 * tpo) {
+            float xv[8], wv[8];
+            load8(xr + i, xv);
+            load8(wr + i, wv);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc += xv[q] * wv[q];
+        }
+        for (int m = 1; m < tpo; m <<= 1) acc += __shfl_xor(acc, m);
+        if (part == 0) a.Qr[(((int64_t)b * a.G + g) * a.k + r) * a.d + c] = (bf16)(acc * a.qscale);
+    }
 }
 
 struct DecodeArgs {

@@ -714,16 +714,29 @@ gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, co
         sl.add(Wv, c.G * c.d, at(ws, L.Vn), OUT_ROWS, (int64_t)c.G * c.d, nullptr);
         run_proj(t, sl, st);
     }
-    hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)t.nC), dim3(256), 0, st, (const float*)lg, idx, w,
-                       (int32_t*)at(ws, F.hist), t.N, t.G, t.M, t.k, 1);
-    int32_t* cbase = (int32_t*)at(ws, F.cbase);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, (const int32_t*)at(ws, F.hist), cbase,
-                       (int32_t*)at(ws, F.offsets), (int32_t*)nullptr, (int)t.nC, t.E);
-    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)t.nC), dim3(256), 0, st, (const int32_t*)idx,
-                       (const int32_t*)cbase, (int32_t*)at(ws, F.perm), (int32_t*)at(ws, F.dst), t.N, t.G, t.M, t.k);
-    run_grouped_q(t, x, Wq, at(ws, F.Qr), (const int32_t*)at(ws, F.perm), (const int32_t*)at(ws, F.dst), cbase, st);
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)(c.B * c.G)), dim3(64), 0, st, (const bf16*)at(ws, L.Kn),
-                       (const bf16*)at(ws, L.Vn), pos, (bf16*)k_cache, (bf16*)vt_cache, c.T, (int)c.B, c.G, c.d);
+    {
+        DecTokArgs ta;
+        ta.logits = lg;
+        ta.x = (const bf16*)x;
+        ta.Wq = (const bf16*)Wq;
+        ta.Kn = (const bf16*)at(ws, L.Kn);
+        ta.Vn = (const bf16*)at(ws, L.Vn);
+        ta.pos = pos;
+        ta.idx = idx;
+        ta.w = w;
+        ta.Qr = (bf16*)at(ws, F.Qr);
+        ta.kc = (bf16*)k_cache;
+        ta.vtc = (bf16*)vt_cache;
+        ta.T = c.T;
+        ta.D = c.D;
+        ta.Bt = (int)c.B;
+        ta.G = c.G;
+        ta.M = c.M;
+        ta.k = c.k;
+        ta.d = c.d;
+        ta.qscale = q_scale(c);
+        hipLaunchKernelGGL(decode_token_kernel, dim3((unsigned)(c.B * c.G)), dim3(256), 0, st, ta);
+    }
     mk.at(1);
     DecodeArgs a;
     a.Qr = (const bf16*)at(ws, F.Qr);

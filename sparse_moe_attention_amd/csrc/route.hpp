@@ -25,6 +25,31 @@ namespace gqe {
 
 constexpr int kChunk = 256;   // tokens per routing chunk (= workgroup size)
 
+// One group of one token: the k best of its M logits (descending, ties to the
+// lower index) and their softmax probabilities over the group.
+__device__ inline void topk_group(const float* zg, int M, int k, int32_t* sel, float* prob) {
+    float mx = -INFINITY;
+    for (int m = 0; m < M; ++m) mx = fmaxf(mx, zg[m]);
+    float se = 0.f;
+    for (int m = 0; m < M; ++m) se += expf(zg[m] - mx);
+    uint64_t taken = 0;
+    for (int r = 0; r < k; ++r) {
+        int best = -1;
+        float bv = -INFINITY;
+        for (int m = 0; m < M; ++m) {
+            if ((taken >> m) & 1ull) continue;
+            const float v = zg[m];
+            if (best < 0 || v > bv) {   // strict: ties keep the lower index
+                best = m;
+                bv = v;
+            }
+        }
+        taken |= 1ull << best;
+        sel[r] = best;
+        prob[r] = expf(bv - mx) / se;
+    }
+}
+
 // MODE 0: route from fp32 logits [N, G*M] -> idx, w and the histogram
 // (renorm = 0: w is the pick's probability, not renormalised).
 // MODE 1: histogram of a caller-given idx (entries outside [0, M), and repeats
@@ -45,29 +70,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* logits, int32_t
             float* wrow = w + n * GK;
             float total = 0.f;
             for (int g = 0; g < G; ++g) {
-                const float* zg = z + g * M;
-                float mx = -INFINITY;
-                for (int m = 0; m < M; ++m) mx = fmaxf(mx, zg[m]);
-                float se = 0.f;
-                for (int m = 0; m < M; ++m) se += expf(zg[m] - mx);
-                uint64_t taken = 0;
+                topk_group(z + g * M, M, k, irow + g * k, wrow + g * k);
                 for (int r = 0; r < k; ++r) {
-                    int best = -1;
-                    float bv = -INFINITY;
-                    for (int m = 0; m < M; ++m) {
-                        if ((taken >> m) & 1ull) continue;
-                        const float v = zg[m];
-                        if (best < 0 || v > bv) {   // strict: ties keep the lower index
-                            best = m;
-                            bv = v;
-                        }
-                    }
-                    taken |= 1ull << best;
-                    const float p = expf(bv - mx) / se;
-                    irow[g * k + r] = best;
-                    wrow[g * k + r] = p;
-                    total += p;
-                    atomicAdd(&h_lds[g * M + best], 1);
+                    total += wrow[g * k + r];
+                    atomicAdd(&h_lds[g * M + irow[g * k + r]], 1);
                 }
             }
             if (renorm) {
