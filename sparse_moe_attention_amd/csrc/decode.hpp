@@ -4,9 +4,11 @@
 // Experts" explainer, technical summary, "Architecture and routing";
 // FrontiersMind GQE article, part 4). Reading the cache dominates, so the
 // attention kernel is an HBM stream:
-//   * decode_token_kernel: per (sequence, group), the group's routing, the
-//     picked experts' queries, and the new key row and value column appended
-//     to the cache;
+//   * the token projections (K, V, shared query, router logits) by
+//     skinny_proj_kernel, one pass over the weights;
+//   * decode_token_kernel: per (sequence, group, rank, 16 query columns), the
+//     group's routing and the picked expert's query; it also appends the new
+//     key row and value column to the cache;
 //   * attn_decode_kernel: one workgroup per (sequence, group, chunk of cached
 //     keys); each wave streams its keys straight from HBM into MFMA operands
 //     (K rows as the A operand of S^T = K Q^T, V^T rows as the A operand of
@@ -15,22 +17,26 @@
 //     online softmax, and writes the chunk's (max, sum, unnormalised output);
 //   * decode_combine_kernel: merges the chunks of every head into its slot of
 //     C = [hard | weighted | shared] (the weighted slot is then formed by the
-//     prefill's combine kernel) for the output projection.
+//     prefill's combine kernel) for the output projection, again a
+//     skinny_proj_kernel pass.
 // The cache layout is the prefill's: keys [G][B][T][d] (one contiguous row
 // per key), values transposed [G][d][B*T] (contiguous keys per column).
 #pragma once
 
 #include "attention.hpp"
+#include "gemm.hpp"
 #include "route.hpp"
 
 namespace gqe {
 
-// Token side of one (sequence b, group g), one workgroup each: the group's
-// top-k from the router logits (as route_kernel picks them), the queries of
-// the picked experts Qr[b][g*k + r] = x[b] Wq_e^T (pre-scaled), and the new
-// key row and value column appended to the cache at pos[b]. Workgroup
-// (b, 0) also writes the token's full routing (idx, renormalised w).
-// 256 threads: 256 / d lanes per output column, each a strided share of D.
+// Token side, one workgroup per (sequence b, group g, rank r, block cb of 16
+// query columns): the group's top-k from the router logits (as route_kernel
+// picks them), then columns 16cb .. 16cb+15 of the picked expert's query
+// Qr[b][g*k + r] = x[b] Wq_e^T (pre-scaled), one pass over those Wq rows as in
+// skinny_proj_kernel (every product column is token b; lanes of column 0
+// store). Workgroups with r = 0 and cb = 0 also append the new key row and
+// value column at pos[b]; workgroup (b, 0, 0, 0) writes the token's full
+// routing (idx, renormalised w).
 struct DecTokArgs {
     const float* logits;  // [B, G*M]
     const bf16* x;        // [B, D]
@@ -48,47 +54,42 @@ struct DecTokArgs {
     float qscale;
 };
 
+template <int MM>   // as in route_kernel
 __global__ __launch_bounds__(256) void decode_token_kernel(DecTokArgs a) {
     __shared__ int32_t s_sel[64];
-    __shared__ float s_prob[64];
-    const int b = blockIdx.x / a.G, g = blockIdx.x % a.G, tid = threadIdx.x;
+    __shared__ f32x4 part[3][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int ncb = a.d / 16;
+    int u = blockIdx.x;
+    const int cb = u % ncb;
+    u /= ncb;
+    const int r = u % a.k;
+    u /= a.k;
+    const int g = u % a.G, b = u / a.G;
     const float* z = a.logits + (int64_t)b * a.G * a.M;
     if (tid == 0) {
-        topk_group(z + g * a.M, a.M, a.k, s_sel, s_prob);
-        if (g == 0) {   // the whole token's routing: the same picks and weights as route_kernel
-            int32_t* irow = a.idx + (int64_t)b * a.G * a.k;
-            float* wrow = a.w + (int64_t)b * a.G * a.k;
-            float total = 0.f;
-            for (int gg = 0; gg < a.G; ++gg) {
-                topk_group(z + gg * a.M, a.M, a.k, irow + gg * a.k, wrow + gg * a.k);
-                for (int r = 0; r < a.k; ++r) total += wrow[gg * a.k + r];
-            }
-            const float inv = 1.f / total;
-            for (int q = 0; q < a.G * a.k; ++q) wrow[q] = wrow[q] * inv;
-        }
+        topk_group<MM>(z + g * a.M, a.M, a.k, [&](int rr, int m, float) { s_sel[rr] = m; });
+        if (g == 0 && r == 0 && cb == 0)   // the whole token's routing: the same picks and weights as route_kernel
+            route_token<MM>(z, a.G, a.M, a.k, 1, a.idx + (int64_t)b * a.G * a.k, a.w + (int64_t)b * a.G * a.k,
+                            [](int) {});
     }
     const int64_t p = a.pos[b];
-    if (tid < a.d && p >= 0 && p < a.T) {
+    if (r == 0 && cb == 0 && tid < a.d && p >= 0 && p < a.T) {
         const int64_t src = ((int64_t)b * a.G + g) * a.d + tid;
         a.kc[(((int64_t)g * a.Bt + b) * a.T + p) * a.d + tid] = a.Kn[src];
         a.vtc[((int64_t)g * a.d + tid) * ((int64_t)a.Bt * a.T) + (int64_t)b * a.T + p] = a.Vn[src];
     }
     __syncthreads();
-    const int tpo = 256 / a.d, c = tid / tpo, part = tid % tpo;   // tpo lanes per output column
-    const bf16* xr = a.x + (int64_t)b * a.D;
-    for (int r = 0; r < a.k; ++r) {
-        const bf16* wr = a.Wq + ((int64_t)(g * a.M + s_sel[r]) * a.d + c) * a.D;
-        float acc = 0.f;
-        for (int64_t i = 8 * part; i < a.D; i += 8 * tpo) {
-            float xv[8], wv[8];
-            load8(xr + i, xv);
-            load8(wr + i, wv);
+    const int e = g * a.M + s_sel[r];
+    const bf16* wrow = a.Wq + ((int64_t)e * a.d + cb * 16 + l16) * a.D;
+    f32x4 acc = skinny_dot(wrow, a.x + (int64_t)b * a.D, (int)a.D, wave, q4);
+    if (!skinny_reduce(acc, part, wave, lane) || l16 != 0) return;
+    bf16x4 q;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc += xv[q] * wv[q];
-        }
-        for (int m = 1; m < tpo; m <<= 1) acc += __shfl_xor(acc, m);
-        if (part == 0) a.Qr[(((int64_t)b * a.G + g) * a.k + r) * a.d + c] = (bf16)(acc * a.qscale);
-    }
+    for (int v = 0; v < 4; ++v) q[v] = (bf16)(acc[v] * a.qscale);
+    *reinterpret_cast<bf16x4*>(a.Qr + (((int64_t)b * a.G + g) * a.k + r) * a.d + cb * 16 + 4 * q4) = q;
 }
 
 struct DecodeArgs {
@@ -265,29 +266,46 @@ void attn_decode_kernel(DecodeArgs a) {
 // Merges the chunks of one head of one sequence (workgroup (b, j): routed
 // head j = g*k + r, or j = G*k for the shared head) and writes its slot of
 // C[b] = [O_0 .. O_{Gk-1} | weighted | O_sh] in bf16. The weighted slot is
-// formed afterwards from the bf16 hard slots, as in the prefill.
+// formed afterwards from the bf16 hard slots, as in the prefill. One wave:
+// the lanes read the chunks' (max, sum) pairs 64 at a time, then lane c sums
+// column c of the chunks' outputs with eight chunks' loads in flight.
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* part_o, const float* part_ml,
                                                             const int32_t* pos, bf16* C, int G, int k, int s0, int d,
                                                             int n_ch, int R16, int64_t ldc, int64_t T) {
     const int GK = G * k;
-    const int b = blockIdx.x / (GK + 1), j = blockIdx.x % (GK + 1), c = threadIdx.x;
-    if (c >= d) return;
+    const int b = blockIdx.x / (GK + 1), j = blockIdx.x % (GK + 1), lane = threadIdx.x;
     const int64_t p = pos[b];
     // An out-of-range position reads no chunk (its slots are unspecified).
     const int64_t len = (p < 0 || p >= T) ? 0 : p + 1;
     const int nch = (int)min<int64_t>(n_ch, (len + kDecCH - 1) / kDecCH);
+    if (nch == 0) return;
     const int g = j < GK ? j / k : s0, hd = j < GK ? j % k : k;   // the shared head is group s0's row k
     const int64_t hb = (((int64_t)b * G + g) * n_ch) * R16 + hd;
+    const float* ml = part_ml + hb * 2;
+    const int64_t mls = (int64_t)R16 * 2;
     float M = -INFINITY;
-    for (int i = 0; i < nch; ++i) M = fmaxf(M, part_ml[(hb + (int64_t)i * R16) * 2]);
-    float so = 0.f, sl = 0.f;
-    for (int i = 0; i < nch; ++i) {
-        const int64_t h = hb + (int64_t)i * R16;
-        const float f = __builtin_amdgcn_exp2f(part_ml[h * 2] - M);
-        so += f * part_o[h * d + c];
-        sl += f * part_ml[h * 2 + 1];
+    for (int i = lane; i < nch; i += 64) M = vmax(M, ml[i * mls]);
+    for (int o = 32; o > 0; o >>= 1) M = vmax(M, __shfl_xor(M, o));
+    float sl = 0.f;
+    for (int i = lane; i < nch; i += 64) sl += __builtin_amdgcn_exp2f(ml[i * mls] - M) * ml[i * mls + 1];
+    for (int o = 32; o > 0; o >>= 1) sl += __shfl_xor(sl, o);
+    if (lane >= d) return;
+    const float* po = part_o + hb * d + lane;
+    const int64_t pos_ = (int64_t)R16 * d;
+    float so = 0.f;
+    int i = 0;
+    for (; i + 8 <= nch; i += 8) {
+        float f[8], v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            f[q] = ml[(i + q) * mls];
+            v[q] = po[(i + q) * pos_];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) so += __builtin_amdgcn_exp2f(f[q] - M) * v[q];
     }
-    C[(int64_t)b * ldc + (j < GK ? (int64_t)j : (int64_t)GK + 1) * d + c] = (bf16)(so / sl);
+    for (; i < nch; ++i) so += __builtin_amdgcn_exp2f(ml[i * mls] - M) * po[i * pos_];
+    C[(int64_t)b * ldc + (j < GK ? (int64_t)j : (int64_t)GK + 1) * d + lane] = (bf16)(so / sl);
 }
 
 }  // namespace gqe

@@ -525,6 +525,91 @@ __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ---------------------------------------------------------------------------
+// Projection of a handful of token rows (one decode step): out_s = A W_s^T
+// for M_rows in the tens, where the time is one pass over the weights and
+// the memory latency of that pass. Workgroup = 16 output columns x 16 rows
+// (a.n_tiles_n = column blocks of 16). Its four waves take interleaved
+// 32-wide K steps and issue the loads of up to eight steps at once, so each
+// wave waits for memory about once per 256 elements of K; the four partial
+// blocks are summed in LDS. W is the A operand of the product, so a lane ends
+// with four consecutive output columns of one row. bf16, K a multiple of 32,
+// row-major outputs only (OUT_ROWS, OUT_ROWS_F32 with its optional bias).
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyRows = 16;
+
+__device__ __forceinline__ f32x4 skinny_dot(const bf16* wrow, const bf16* xrow, int K, int wave, int q4) {
+    const int S = K / 32;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = wave; s0 < S; s0 += 32) {
+        Frag<bf16> wf[8], xf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = s0 + 4 * j;
+            if (s < S) {
+                wf[j] = ld_frag<bf16>(wrow + s * 32 + 8 * q4);
+                xf[j] = ld_frag<bf16>(xrow + s * 32 + 8 * q4);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s0 + 4 * j < S) acc = mma16(wf[j], xf[j], acc);
+    }
+    return acc;
+}
+
+// Sum of the four waves' blocks, left in wave 0 (the other waves return false).
+__device__ __forceinline__ bool skinny_reduce(f32x4& acc, f32x4 (&part)[3][64], int wave, int lane) {
+    if (wave > 0) part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave > 0) return false;
+    acc += part[0][lane];
+    acc += part[1][lane];
+    acc += part[2][lane];
+    return true;
+}
+
+__global__ __launch_bounds__(256) void skinny_proj_kernel(ProjArgs a) {
+    __shared__ f32x4 part[3][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int n0 = (int)(blockIdx.x % a.n_tiles_n) * 16;
+    const int64_t m0 = (int64_t)(blockIdx.x / a.n_tiles_n) * kSkinnyRows;
+    // Weight row of output column n0 + l16 (columns past every block read a
+    // valid row whose results are dropped), activation row of token m0 + l16.
+    const bf16* wrow = (const bf16*)a.seg[0].W;
+    for (int s = 0; s < a.n_segs; ++s) {
+        const int c = n0 + l16 - a.seg[s].col_begin;
+        if (c >= 0 && c < a.seg[s].n_cols) wrow = (const bf16*)a.seg[s].W + (int64_t)c * a.K;
+    }
+    const int64_t m = m0 + l16;
+    const bf16* xrow = (const bf16*)a.A + (m < a.M_rows ? m : m0) * a.lda;
+    f32x4 acc = skinny_dot(wrow, xrow, a.K, wave, q4);
+    if (!skinny_reduce(acc, part, wave, lane) || m >= a.M_rows) return;
+    const int n = n0 + 4 * q4;   // a block starts at a multiple of 8: the four columns share it
+    for (int s = 0; s < a.n_segs; ++s) {
+        const ProjSeg& sg = a.seg[s];
+        const int c = n - sg.col_begin;
+        if (c < 0 || c >= sg.n_cols) continue;
+        const f32x4 v = acc * sg.scale;
+        if (sg.mode == OUT_ROWS_F32) {
+            float* o = (float*)sg.out + m * sg.ld_out + c;
+            for (int q = 0; q < 4 && c + q < sg.n_cols; ++q) o[q] = v[q] + (sg.bias ? sg.bias[c + q] : 0.f);
+        } else {
+            bf16* o = (bf16*)sg.out + m * sg.ld_out + c;
+            if (c + 4 <= sg.n_cols && (sg.ld_out & 3) == 0 && (reinterpret_cast<uintptr_t>(sg.out) & 7) == 0) {
+                bf16x4 w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = (bf16)v[q];
+                *reinterpret_cast<bf16x4*>(o) = w;
+            } else {
+                for (int q = 0; q < 4 && c + q < sg.n_cols; ++q) o[q] = (bf16)v[q];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Sparse Q projection as a grouped GEMM. Expert e's picks form the segment
 // [cbase[0][e], cbase[nC][e]) of the permutation, in token order; a
 // workgroup takes BM consecutive rows of one segment (tile t of expert e),

@@ -184,6 +184,36 @@ void run_proj(const Dims& d, SegList& sl, hipStream_t st) {
     else launch_proj<bf16, ProjBf16>(sl.a, sl.cols, st);
 }
 
+// A projection of at most kSkinnyMaxRows token rows (a decode step) in bf16:
+// skinny_proj_kernel, one pass over the weights; larger ones take the tiled
+// GEMM. Row-major outputs only, K a multiple of 32 (the callers' D and slot
+// widths are).
+constexpr int64_t kSkinnyMaxRows = 64;
+void run_proj_rows(const Dims& d, SegList& sl, hipStream_t st) {
+    if (d.f32 || sl.a.M_rows > kSkinnyMaxRows || sl.a.K % 32 != 0) {
+        run_proj(d, sl, st);
+        return;
+    }
+    sl.a.n_tiles_n = (sl.cols + 15) / 16;
+    const int64_t n_m = (sl.a.M_rows + kSkinnyRows - 1) / kSkinnyRows;
+    hipLaunchKernelGGL(skinny_proj_kernel, dim3((unsigned)(n_m * sl.a.n_tiles_n)), dim3(256), 0, st, sl.a);
+}
+
+// Routing from the logits (route_kernel<0>): group widths 1, 2, 4, 8 and 16
+// have their logits loaded into registers at once, others read them one by one.
+void run_route(const Dims& d, const float* lg, int32_t* idx, float* w, int32_t* hist, hipStream_t st) {
+    const int renorm = d.variant != GQE_WEIGHTED_CONCAT;
+    const dim3 grid((unsigned)d.nC), blk(256);
+    switch (d.M) {
+        case 1: hipLaunchKernelGGL((route_kernel<0, 1>), grid, blk, 0, st, lg, idx, w, hist, d.N, d.G, d.M, d.k, renorm); break;
+        case 2: hipLaunchKernelGGL((route_kernel<0, 2>), grid, blk, 0, st, lg, idx, w, hist, d.N, d.G, d.M, d.k, renorm); break;
+        case 4: hipLaunchKernelGGL((route_kernel<0, 4>), grid, blk, 0, st, lg, idx, w, hist, d.N, d.G, d.M, d.k, renorm); break;
+        case 8: hipLaunchKernelGGL((route_kernel<0, 8>), grid, blk, 0, st, lg, idx, w, hist, d.N, d.G, d.M, d.k, renorm); break;
+        case 16: hipLaunchKernelGGL((route_kernel<0, 16>), grid, blk, 0, st, lg, idx, w, hist, d.N, d.G, d.M, d.k, renorm); break;
+        default: hipLaunchKernelGGL((route_kernel<0, 0>), grid, blk, 0, st, lg, idx, w, hist, d.N, d.G, d.M, d.k, renorm);
+    }
+}
+
 // Queries are stored pre-multiplied by log2(e)/sqrt(d): the attention kernel
 // then works in log2 units with no per-score scaling.
 float q_scale(const Dims& d) { return (float)(1.4426950408889634 / std::sqrt((double)d.d)); }
@@ -635,8 +665,7 @@ gqe_status fwd_impl(const gqe_shape* s, const void* x, const void* Wr, const flo
     sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
     run_proj(d, sl, st);
     mk.at(1);
-    hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)lg, idx, w,
-                       (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k, (int)(d.variant != GQE_WEIGHTED_CONCAT));
+    run_route(d, lg, idx, w, (int32_t*)at(ws, L.hist), st);
     rc = run_post_router(d, L, ws, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, at(ws, L.C), st, false, mk,
                          train ? (float*)at(ws, TL.lse) : nullptr, TL.rs.Lr, TL.rs.Lx);
     if (rc != GQE_OK || !train) return rc;
@@ -712,7 +741,7 @@ gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, co
         sl.add(Wq_sh, c.d, at(ws, F.Qsh), OUT_ROWS, c.d, nullptr, q_scale(c));
         sl.add(Wr, c.E, lg, OUT_ROWS_F32, c.E, br);
         sl.add(Wv, c.G * c.d, at(ws, L.Vn), OUT_ROWS, (int64_t)c.G * c.d, nullptr);
-        run_proj(t, sl, st);
+        run_proj_rows(t, sl, st);
     }
     {
         DecTokArgs ta;
@@ -735,7 +764,15 @@ gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, co
         ta.k = c.k;
         ta.d = c.d;
         ta.qscale = q_scale(c);
-        hipLaunchKernelGGL(decode_token_kernel, dim3((unsigned)(c.B * c.G)), dim3(256), 0, st, ta);
+        const dim3 grid((unsigned)(c.B * c.G * c.k * (c.d / 16))), blk(256);
+        switch (c.M) {
+            case 1: hipLaunchKernelGGL(decode_token_kernel<1>, grid, blk, 0, st, ta); break;
+            case 2: hipLaunchKernelGGL(decode_token_kernel<2>, grid, blk, 0, st, ta); break;
+            case 4: hipLaunchKernelGGL(decode_token_kernel<4>, grid, blk, 0, st, ta); break;
+            case 8: hipLaunchKernelGGL(decode_token_kernel<8>, grid, blk, 0, st, ta); break;
+            case 16: hipLaunchKernelGGL(decode_token_kernel<16>, grid, blk, 0, st, ta); break;
+            default: hipLaunchKernelGGL(decode_token_kernel<0>, grid, blk, 0, st, ta);
+        }
     }
     mk.at(1);
     DecodeArgs a;
@@ -766,7 +803,7 @@ gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, co
     run_combine(t, C, w, st);
     SegList so = proj_base(t, C, ldc, t.N, (int)ldc);
     so.add(Wo, (int)c.D, out, OUT_ROWS, c.D, nullptr);
-    run_proj(t, so, st);
+    run_proj_rows(t, so, st);
     mk.at(3);
     return last_hip();
 }
@@ -798,8 +835,7 @@ gqe_status gqe_route(const gqe_shape* s, const void* x, const void* Wr, const fl
     sl.add(Wr, d.E, lg, OUT_ROWS_F32, d.E, br);
     run_proj(d, sl, st);
     int32_t* hist = (int32_t*)at(ws, L.hist);
-    hipLaunchKernelGGL((route_kernel<0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)lg, idx, w, hist,
-                       d.N, d.G, d.M, d.k, (int)(d.variant != GQE_WEIGHTED_CONCAT));
+    run_route(d, lg, idx, w, hist, st);
     if (counts)
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, (const int32_t*)hist,
                            (int32_t*)at(ws, L.cbase), (int32_t*)at(ws, L.offsets), counts, (int)d.nC, d.E);
@@ -821,7 +857,7 @@ gqe_status gqe_attn_fwd_routed(const gqe_shape* s, const void* x, const void* Wq
     const GqeWs L = gqe_layout(d);
     if (ws_bytes < L.total) return GQE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL((route_kernel<1>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)nullptr,
+    hipLaunchKernelGGL((route_kernel<1, 0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)nullptr,
                        const_cast<int32_t*>(idx), (float*)nullptr, (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k, 1);
     void* C = slots_out ? slots_out : at(ws, L.C);
     return run_post_router(d, L, ws, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, C, st, true, Marks{nullptr, st});

@@ -26,37 +26,71 @@ namespace gqe {
 constexpr int kChunk = 256;   // tokens per routing chunk (= workgroup size)
 
 // One group of one token: the k best of its M logits (descending, ties to the
-// lower index) and their softmax probabilities over the group.
-__device__ inline void topk_group(const float* zg, int M, int k, int32_t* sel, float* prob) {
+// lower index) and their softmax probabilities over the group, passed to
+// emit(r, m, p) in rank order. MM > 0: M == MM, and the logits are loaded
+// once, all together, into registers; MM == 0: any M <= 64, read through zg.
+// Both give the same values (same operations in the same order).
+template <int MM, class Emit>
+__device__ inline void topk_group(const float* zg, int M, int k, Emit&& emit) {
+    float zr[MM > 0 ? MM : 1];
+    if constexpr (MM > 0) {
+#pragma unroll
+        for (int m = 0; m < MM; ++m) zr[m] = zg[m];
+    }
+    auto z = [&](int m) -> float {
+        if constexpr (MM > 0) return zr[m];
+        else return zg[m];
+    };
+    const int Mg = MM > 0 ? MM : M;
     float mx = -INFINITY;
-    for (int m = 0; m < M; ++m) mx = fmaxf(mx, zg[m]);
+    for (int m = 0; m < Mg; ++m) mx = fmaxf(mx, z(m));
     float se = 0.f;
-    for (int m = 0; m < M; ++m) se += expf(zg[m] - mx);
+    for (int m = 0; m < Mg; ++m) se += expf(z(m) - mx);
     uint64_t taken = 0;
     for (int r = 0; r < k; ++r) {
         int best = -1;
         float bv = -INFINITY;
-        for (int m = 0; m < M; ++m) {
+        for (int m = 0; m < Mg; ++m) {
             if ((taken >> m) & 1ull) continue;
-            const float v = zg[m];
+            const float v = z(m);
             if (best < 0 || v > bv) {   // strict: ties keep the lower index
                 best = m;
                 bv = v;
             }
         }
         taken |= 1ull << best;
-        sel[r] = best;
-        prob[r] = expf(bv - mx) / se;
+        emit(r, best, expf(bv - mx) / se);
     }
 }
 
+// The routing of one token from its logits row z [G*M]: idx row [G*k] and
+// weights w row [G*k], each written once (a first pass over the groups sums
+// the picks' probabilities for the renormalisation, a second writes); also
+// calls count(e) for every pick's expert e = g*M + m.
+template <int MM, class Count>
+__device__ inline void route_token(const float* z, int G, int M, int k, int renorm, int32_t* irow, float* wrow,
+                                   Count&& count) {
+    float total = 0.f;
+    if (renorm)
+        for (int g = 0; g < G; ++g) topk_group<MM>(z + g * M, M, k, [&](int, int, float p) { total += p; });
+    const float inv = renorm ? 1.f / total : 1.f;
+    for (int g = 0; g < G; ++g)
+        topk_group<MM>(z + g * M, M, k, [&](int r, int m, float p) {
+            irow[g * k + r] = m;
+            wrow[g * k + r] = renorm ? p * inv : p;
+            count(g * M + m);
+        });
+}
+
 // MODE 0: route from fp32 logits [N, G*M] -> idx, w and the histogram
-// (renorm = 0: w is the pick's probability, not renormalised).
+// (renorm = 0: w is the pick's probability, not renormalised). MM as in
+// topk_group.
 // MODE 1: histogram of a caller-given idx (entries outside [0, M), and repeats
 // of an earlier rank's expert in the same group, are skipped).
-template <int MODE>
-__global__ __launch_bounds__(256) void route_kernel(const float* logits, int32_t* idx, float* w,
-                                                    int32_t* hist, int64_t N, int G, int M, int k, int renorm) {
+template <int MODE, int MM>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int32_t* __restrict__ idx,
+                                                    float* __restrict__ w, int32_t* __restrict__ hist, int64_t N,
+                                                    int G, int M, int k, int renorm) {
     __shared__ int32_t h_lds[256];
     const int E = G * M;
     for (int e = threadIdx.x; e < E; e += 256) h_lds[e] = 0;
@@ -66,20 +100,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* logits, int32_t
     if (n < N) {
         int32_t* irow = idx + n * GK;
         if (MODE == 0) {
-            const float* z = logits + n * E;
-            float* wrow = w + n * GK;
-            float total = 0.f;
-            for (int g = 0; g < G; ++g) {
-                topk_group(z + g * M, M, k, irow + g * k, wrow + g * k);
-                for (int r = 0; r < k; ++r) {
-                    total += wrow[g * k + r];
-                    atomicAdd(&h_lds[g * M + irow[g * k + r]], 1);
-                }
-            }
-            if (renorm) {
-                const float inv = 1.f / total;
-                for (int q = 0; q < GK; ++q) wrow[q] = wrow[q] * inv;
-            }
+            route_token<MM>(logits + n * E, G, M, k, renorm, irow, w + n * GK,
+                            [&](int e) { atomicAdd(&h_lds[e], 1); });
         } else {
             for (int g = 0; g < G; ++g)
                 for (int r = 0; r < k; ++r) {
@@ -149,42 +171,55 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* hist, int32_t
 // token's rank is the number of earlier tokens of its wave that picked e
 // (wave ballot) plus the totals of the earlier waves (one LDS exchange).
 // perm = token, dst = row of the dense [N, G, k] layout (the first rank r at
-// which the token picked e). Two passes over the experts: count, then write.
-__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* idx, const int32_t* cbase, int32_t* perm,
-                                                      int32_t* dst, int64_t N, int G, int M, int k) {
+// which the token picked e). Two passes over the groups: count, then write;
+// each takes a group's picks as a bit mask over its M experts (picks outside
+// [0, M) are skipped, as route_kernel<1> skips them).
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ cbase,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ dst, int64_t N,
+                                                      int G, int M, int k) {
     __shared__ int32_t wtot[4][256];           // picks of expert e in each wave of the chunk
+    __shared__ int32_t base[256];              // this chunk's first permutation row of each expert
     const int E = G * M;
     const int tid = threadIdx.x, wave = tid >> 6;
+    for (int e = tid; e < E; e += 256) base[e] = cbase[(int64_t)blockIdx.x * E + e];
     const int64_t n = (int64_t)blockIdx.x * kChunk + tid;
     const bool valid = n < N;
     const int GK = G * k;
     const int32_t* row = idx + (valid ? n : 0) * GK;
-    // r at which this token picked expert m of group g, or -1.
-    auto pick_rank = [&](int g, int m) {
-        int hit = -1;
-        if (valid)
-            for (int r = k - 1; r >= 0; --r)
-                if (row[g * k + r] == m) hit = r;
-        return hit;
+    auto group_mask = [&](int g) -> uint64_t {
+        uint64_t pm = 0;
+        if (valid) {
+#pragma unroll 4
+            for (int r = 0; r < k; ++r) {
+                const int m = row[g * k + r];
+                if (m >= 0 && m < M) pm |= 1ull << m;
+            }
+        }
+        return pm;
     };
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+        const uint64_t pm = group_mask(g);
         for (int m = 0; m < M; ++m) {
-            const uint64_t mask = __builtin_amdgcn_ballot_w64(pick_rank(g, m) >= 0);
+            const uint64_t mask = __builtin_amdgcn_ballot_w64((pm >> m) & 1ull);
             if ((tid & 63) == 0) wtot[wave][g * M + m] = __builtin_popcountll(mask);
         }
+    }
     __syncthreads();
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+        const uint64_t pm = group_mask(g);
         for (int m = 0; m < M; ++m) {
-            const int r = pick_rank(g, m);
-            const uint64_t mask = __builtin_amdgcn_ballot_w64(r >= 0);
-            if (r < 0) continue;
+            const uint64_t mask = __builtin_amdgcn_ballot_w64((pm >> m) & 1ull);
+            if (!((pm >> m) & 1ull)) continue;
             const int e = g * M + m;
-            int pos = cbase[(int64_t)blockIdx.x * E + e];
+            int pos = base[e];
             for (int w = 0; w < wave; ++w) pos += wtot[w][e];
             pos += __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+            int r = 0;
+            while (row[g * k + r] != m) ++r;            // the first rank that picked m (bit set: one exists)
             perm[pos] = (int32_t)n;
             dst[pos] = (int32_t)(n * GK + g * k + r);
         }
+    }
 }
 
 // Weighted slot: C[n, GK*d + c] = sum_s w[n, s] * C[n, s*d + c] over the GK
@@ -199,22 +234,29 @@ __global__ __launch_bounds__(256) void combine_kernel(T* C, const float* w, int6
     if (i >= N * chunks) return;
     const int64_t n = i / chunks;
     const int c = (int)(i % chunks) * 8;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     T* row = C + n * ldc;
+    if (scale_in_place) {
+        for (int s = 0; s < GK; ++s) {
+            const float ws = w[n * GK + s];
+            float v[8];
+            load8<T>(row + s * d + c, v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= ws;
+            store8<T>(row + s * d + c, v);
+        }
+        return;
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // Slots in ascending order; four slots' loads in flight at a time.
+#pragma unroll 4
     for (int s = 0; s < GK; ++s) {
         const float ws = w[n * GK + s];
         float v[8];
         load8<T>(row + s * d + c, v);
-        if (scale_in_place) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] *= ws;
-            store8<T>(row + s * d + c, v);
-            continue;
-        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] += ws * v[q];
     }
-    if (!scale_in_place) store8<T>(row + (int64_t)GK * d + c, acc);
+    store8<T>(row + (int64_t)GK * d + c, acc);
 }
 
 }  // namespace gqe

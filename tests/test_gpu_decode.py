@@ -86,3 +86,51 @@ def test_decode_parity(name):
         v_after[:, b, p] = vc[:, b, p]
     assert torch.equal(k_after.view(torch.int16), kc.view(torch.int16)), (name, "key cache changed elsewhere")
     assert torch.equal(v_after.contiguous().view(torch.int16), vc.view(torch.int16)), (name, "value cache changed")
+
+
+def test_decode_parity_at_bench_workload():
+    """The launch the benchmark times: 16 sequences x 32767 cached positions
+    of the 32K-token layer (B1 T32768 D1024 G8 M2 k1 d64 per sequence), new
+    token at position 32767, the benchmark's seeded inputs. All 16 sequences
+    run; three of them are checked against the oracle (the sequences are
+    independent). Position 32767 holds NaN before the call: it is written,
+    never read."""
+    import dataclasses
+    B, T = 16, 32768
+    s = Shape(B=B, T=T, D=1024, G=8, M=2, k=1, d=64)
+    print(f"[decode bench workload] {s}", flush=True)
+    tok = make_inputs(dataclasses.replace(s, T=1), seed=4000)
+    dv = H.to_device(tok)
+    gen = torch.Generator(device="cuda").manual_seed(4001)
+    kd = torch.randn(s.G, B, T, s.d, device="cuda", generator=gen).to(torch.bfloat16)
+    vtd = torch.randn(s.G, s.d, B * T, device="cuda", generator=gen).to(torch.bfloat16)
+    kd[:, :, T - 1] = float("nan")
+    vtd.view(s.G, s.d, B, T)[:, :, :, T - 1] = float("nan")
+    pos = [T - 1] * B
+    posd = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    sh = gq.shape_from(s)
+    ws = torch.empty(gq.gqe_decode_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, s.D, dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(B, s.G, s.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(B, s.G, s.k, dtype=torch.float32, device="cuda")
+    gq.gqe_decode_step(sh, posd, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"], dv["Wo"],
+                       kd, vtd, out, ws, idx, w)
+    torch.cuda.synchronize()
+
+    sel = [0, 9, 15]
+    f = H.f64_inputs(tok)
+    f_sel = dict(f, x=f["x"][sel])
+    k64 = kd[:, sel].float().cpu().numpy().astype(np.float64).transpose(1, 0, 2, 3)   # [3, G, T, d]
+    v64 = vtd.view(s.G, s.d, B, T)[:, :, sel].float().cpu().numpy().astype(np.float64).transpose(2, 0, 3, 1)
+    ref = gd.gqe_decode(f_sel, k64, v64, [T - 1] * len(sel), s.G, s.M, s.k, s.d)
+    assert (idx.cpu().numpy()[sel] == ref["idx"]).all(), "routing"
+    got = H.np32(out)[sel]
+    err, bound = H.out_error(got, ref["out"])
+    assert np.isfinite(got).all() and err <= bound, ("out", err, bound)
+    # the appended key row and value column of the checked sequences
+    for i, b in enumerate(sel):
+        err, bound = H.out_error(H.np32(kd[:, b, T - 1]), ref["K_new"][i])
+        assert err <= bound, ("appended key", b, err, bound)
+        err, bound = H.out_error(H.np32(vtd.view(s.G, s.d, B, T)[:, :, b, T - 1]), ref["V_new"][i])
+        assert err <= bound, ("appended value", b, err, bound)
+    assert torch.isfinite(out.float()).all()
