@@ -56,7 +56,9 @@ struct DecTokArgs {
 
 template <int MM>   // as in route_kernel
 __global__ __launch_bounds__(256) void decode_token_kernel(DecTokArgs a) {
-    __shared__ int32_t s_sel[64];
+    __shared__ int32_t s_sel[256];   // token b's picks [g*k + r] (G*k <= 256)
+    __shared__ float s_p[256];       // and their probabilities within the group
+    __shared__ float s_inv;
     __shared__ f32x4 part[3][64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -69,11 +71,27 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecTokArgs a) {
     u /= a.k;
     const int g = u % a.G, b = u / a.G;
     const float* z = a.logits + (int64_t)b * a.G * a.M;
-    if (tid == 0) {
-        topk_group<MM>(z + g * a.M, a.M, a.k, [&](int rr, int m, float) { s_sel[rr] = m; });
-        if (g == 0 && r == 0 && cb == 0)   // the whole token's routing: the same picks and weights as route_kernel
-            route_token<MM>(z, a.G, a.M, a.k, 1, a.idx + (int64_t)b * a.G * a.k, a.w + (int64_t)b * a.G * a.k,
-                            [](int) {});
+    // Every group's top-k, one thread per group.
+    for (int gg = tid; gg < a.G; gg += 256)
+        topk_group<MM>(z + gg * a.M, a.M, a.k, [&](int rr, int m, float pr) {
+            s_sel[gg * a.k + rr] = m;
+            s_p[gg * a.k + rr] = pr;
+        });
+    __syncthreads();
+    if (g == 0 && r == 0 && cb == 0) {
+        // The token's routing as route_kernel writes it: the same picks, and
+        // the probabilities renormalised by their sum taken in the same order.
+        const int GK = a.G * a.k;
+        if (tid == 0) {
+            float total = 0.f;
+            for (int q = 0; q < GK; ++q) total += s_p[q];
+            s_inv = 1.f / total;
+        }
+        __syncthreads();
+        for (int q = tid; q < GK; q += 256) {
+            a.idx[(int64_t)b * GK + q] = s_sel[q];
+            a.w[(int64_t)b * GK + q] = s_p[q] * s_inv;
+        }
     }
     const int64_t p = a.pos[b];
     if (r == 0 && cb == 0 && tid < a.d && p >= 0 && p < a.T) {
@@ -81,8 +99,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecTokArgs a) {
         a.kc[(((int64_t)g * a.Bt + b) * a.T + p) * a.d + tid] = a.Kn[src];
         a.vtc[((int64_t)g * a.d + tid) * ((int64_t)a.Bt * a.T) + (int64_t)b * a.T + p] = a.Vn[src];
     }
-    __syncthreads();
-    const int e = g * a.M + s_sel[r];
+    const int e = g * a.M + s_sel[g * a.k + r];
     const bf16* wrow = a.Wq + ((int64_t)e * a.d + cb * 16 + l16) * a.D;
     f32x4 acc = skinny_dot(wrow, a.x + (int64_t)b * a.D, (int)a.D, wave, q4);
     if (!skinny_reduce(acc, part, wave, lane) || l16 != 0) return;
