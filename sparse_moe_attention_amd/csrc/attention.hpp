@@ -67,18 +67,24 @@ __device__ __forceinline__ int64_t attn_lse_base(const AttnArgs& a, int g, int b
 }
 
 // Tile shape: queries per wave, waves per workgroup, waves per SIMD the
-// register budget is sized for, keys per tile.
+// register budget is sized for, keys per tile. Four-wave workgroups of 128
+// query rows with 64-key tiles (32 KB of LDS for the two stages) let three
+// workgroups share a CU, three waves per SIMD. The waves that share a SIMD
+// then belong to different workgroups, whose barriers are independent, so
+// one wave's softmax runs while another's products do; with two waves of
+// one eight-wave workgroup per SIMD both met every barrier together and
+// took turns (measured 9% slower at T = 32K, 7% at the k = 2 workload).
 #ifndef GQE_ATTN_QW
 #define GQE_ATTN_QW 32
 #endif
 #ifndef GQE_ATTN_NW
-#define GQE_ATTN_NW 8
+#define GQE_ATTN_NW 4
 #endif
 #ifndef GQE_ATTN_WPE
-#define GQE_ATTN_WPE 2
+#define GQE_ATTN_WPE 3
 #endif
 #ifndef GQE_ATTN_BKV
-#define GQE_ATTN_BKV 128
+#define GQE_ATTN_BKV 64
 #endif
 constexpr int kAttnQW = GQE_ATTN_QW;
 constexpr int kAttnNW = GQE_ATTN_NW;

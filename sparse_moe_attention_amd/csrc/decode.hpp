@@ -137,7 +137,12 @@ template <int D>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(GQE_DEC_WPE)))
 void attn_decode_kernel(DecodeArgs a) {
     constexpr int DK = D / 32, CB = D / 16;
-    constexpr int NB = kDecCW / 32;                 // 32-key steps per wave
+#ifndef GQE_DEC_KS
+#define GQE_DEC_KS 64
+#endif
+    constexpr int KS = GQE_DEC_KS;                  // keys per step
+    constexpr int KB = KS / 16, KH = KS / 32;       // 16-key score blocks, 32-key product steps
+    constexpr int NB = kDecCW / KS;                 // steps per wave
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -176,46 +181,60 @@ void attn_decode_kernel(DecodeArgs a) {
         float m = -INFINITY;                         // running max of head l16 (log2 units)
 
         const int64_t w0 = c0 + (int64_t)wave * kDecCW;
-        const int nb = (int)max<int64_t>(0, min<int64_t>(NB, (len - w0 + 31) / 32));
-        // Operand fragments of one 32-key step: K rows (A of S^T) and V^T rows (A of O^T).
-        auto load = [&](int j, Frag<bf16> (&kf)[2][DK], Frag<bf16> (&vf)[CB]) {
-            const int64_t k0 = w0 + 32 * j;
+        const int nb = (int)max<int64_t>(0, min<int64_t>(NB, (len - w0 + KS - 1) / KS));
+        // Operand fragments of one step of KS keys: K rows (A of S^T) and
+        // V^T rows (A of O^T). Each V^T row's KS keys (128 bytes) are
+        // requested together. Keys past the cache end (the last step of a
+        // sequence whose T is not a multiple of KS) read the last row
+        // instead; they lie past len, so they are masked below.
+        auto load = [&](int j, Frag<bf16> (&kf)[KB][DK], Frag<bf16> (&vf)[KH][CB]) {
+            const int64_t k0 = w0 + (int64_t)KS * j;
+            const bool tail = k0 + KS > a.T;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb) {
+                int64_t kr = k0 + key_of_row(kb, l16);
+                if (tail) kr = min<int64_t>(kr, a.T - 1);
 #pragma unroll
-                for (int dk = 0; dk < DK; ++dk)
-                    kf[kb][dk] = ld_frag<bf16>(Kg + (k0 + key_of_row(kb, l16)) * D + dk * 32 + 8 * q4);
+                for (int dk = 0; dk < DK; ++dk) kf[kb][dk] = ld_frag<bf16>(Kg + kr * D + dk * 32 + 8 * q4);
+            }
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) vf[cb] = ld_frag<bf16>(Vg + (int64_t)(cb * 16 + l16) * vrow + k0 + 8 * q4);
+            for (int h = 0; h < KH; ++h) {
+                int64_t kc = k0 + 32 * h + 8 * q4;
+                if (tail) kc = min<int64_t>(kc, a.T - 8);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) vf[h][cb] = ld_frag<bf16>(Vg + (int64_t)(cb * 16 + l16) * vrow + kc);
+            }
         };
-        Frag<bf16> kA[2][DK], vA[CB], kB[2][DK], vB[CB];
-        auto compute = [&](int j, const Frag<bf16> (&kf)[2][DK], Frag<bf16> (&vf)[CB]) {
-            const int64_t k0 = w0 + 32 * j;
-            f32x4 s[2];
+        Frag<bf16> kA[KB][DK], vA[KH][CB], kB[KB][DK], vB[KH][CB];
+        auto compute = [&](int j, const Frag<bf16> (&kf)[KB][DK], Frag<bf16> (&vf)[KH][CB]) {
+            const int64_t k0 = w0 + (int64_t)KS * j;
+            f32x4 s[KB];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
                 s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int dk = 0; dk < DK; ++dk) s[kb] = mma16(kf[kb][dk], qf[dk], s[kb]);
             }
-            if (k0 + 32 > len) {
+            if (k0 + KS > len) {
                 // Keys at or past len are not attended: their scores become -inf
                 // and their values 0 (the cache there may hold any bits, and a
                 // NaN times a zero probability would still be NaN).
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         if (k0 + key_of_row(kb, 4 * q4 + v) >= len) s[kb][v] = -INFINITY;
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
+                for (int h = 0; h < KH; ++h)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (k0 + 8 * q4 + i >= len) vf[cb].v[i] = (bf16)0.f;
+                    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (k0 + 32 * h + 8 * q4 + i >= len) vf[h][cb].v[i] = (bf16)0.f;
             }
             float mx = s[0][0];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) mx = vmax(mx, s[kb][v]);
             mx = quad_row_max(mx);
@@ -225,16 +244,23 @@ void attn_decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) o[cb] *= corr;
             lsum *= corr;
-            Frag<bf16> pf;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                pf.v[v] = (bf16)__builtin_amdgcn_exp2f(s[0][v] - mn);
-                pf.v[4 + v] = (bf16)__builtin_amdgcn_exp2f(s[1][v] - mn);
+            for (int h = 0; h < KH; ++h) {
+                Frag<bf16> pf;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    pf.v[v] = (bf16)__builtin_amdgcn_exp2f(s[2 * h][v] - mn);
+                    pf.v[4 + v] = (bf16)__builtin_amdgcn_exp2f(s[2 * h + 1][v] - mn);
+                }
+                lsum = mma16(ones, pf, lsum);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) o[cb] = mma16(vf[h][cb], pf, o[cb]);
             }
-            lsum = mma16(ones, pf, lsum);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) o[cb] = mma16(vf[cb], pf, o[cb]);
         };
+#ifndef GQE_DEC_DB
+#define GQE_DEC_DB 1
+#endif
+#if GQE_DEC_DB
         // Two register sets: the next step's loads are in flight during this step's products.
         if (nb > 0) load(0, kA, vA);
         for (int j = 0; j < nb; j += 2) {
@@ -245,6 +271,12 @@ void attn_decode_kernel(DecodeArgs a) {
                 compute(j + 1, kB, vB);
             }
         }
+#else
+        for (int j = 0; j < nb; ++j) {
+            load(j, kA, vA);
+            compute(j, kA, vA);
+        }
+#endif
         // Merge the waves: lane (l16, q4) holds head l16, columns 16cb + 4*q4 + v.
         const float l = __shfl(lsum[0], l16);
         if (q4 == 0) {
