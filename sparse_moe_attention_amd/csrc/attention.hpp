@@ -66,29 +66,28 @@ __device__ __forceinline__ int64_t attn_lse_base(const AttnArgs& a, int g, int b
     return before + (int64_t)b * (xg ? a.lse_Lx : a.lse_Lr);
 }
 
-// Tile shape: queries per wave, waves per workgroup, waves per SIMD the
-// register budget is sized for, keys per tile. Four-wave workgroups of 128
-// query rows with 64-key tiles (32 KB of LDS for the two stages) let three
-// workgroups share a CU, three waves per SIMD. The waves that share a SIMD
-// then belong to different workgroups, whose barriers are independent, so
-// one wave's softmax runs while another's products do; with two waves of
-// one eight-wave workgroup per SIMD both met every barrier together and
-// took turns (measured 9% slower at T = 32K, 7% at the k = 2 workload).
-#ifndef GQE_ATTN_QW
-#define GQE_ATTN_QW 32
-#endif
-#ifndef GQE_ATTN_NW
-#define GQE_ATTN_NW 4
-#endif
-#ifndef GQE_ATTN_WPE
-#define GQE_ATTN_WPE 3
-#endif
-#ifndef GQE_ATTN_BKV
-#define GQE_ATTN_BKV 64
-#endif
-constexpr int kAttnQW = GQE_ATTN_QW;
-constexpr int kAttnNW = GQE_ATTN_NW;
-constexpr int kAttnBKV = GQE_ATTN_BKV;
+// Tile shapes: queries per wave (both), then waves per workgroup, keys per
+// tile and the waves per SIMD the register budget is sized for.
+//   * Short sequences: four-wave workgroups of 128 query rows with 64-key
+//     tiles (32 KB of LDS for the two stages), three workgroups per CU. The
+//     waves that share a SIMD then belong to different workgroups, whose
+//     barriers are independent, so one wave's softmax runs while another's
+//     products do; with two waves of one eight-wave workgroup per SIMD both
+//     met every barrier together and took turns (measured 9% slower at
+//     T = 32K, 7% at the k = 2 workload).
+//   * Long sequences: eight-wave workgroups of 256 rows with 128-key tiles,
+//     one per CU. A query tile reads every K/V tile up to its diagonal, rows
+//     x 4d flops for 4d bytes, so once a group's K/V stream outgrows the
+//     caches (T = 1M: 256 MB per group) 128-row tiles are held near
+//     128 flop/byte x 8 TB/s = 1 PFLOP/s by HBM; 256-row tiles halve those
+//     reads (T = 1M: 1.10 s against 1.48 s per layer).
+constexpr int kAttnQW = 32;
+template <int NW_, int BKV_, int WPE_>
+struct AttnShape {
+    static constexpr int NW = NW_, BKV = BKV_, WPE = WPE_, BQ = NW_ * kAttnQW;
+};
+using AttnShort = AttnShape<4, 64, 3>;
+using AttnLong = AttnShape<8, 128, 2>;
 constexpr float kLazyRescale = 8.f;   // log2 units the running max may lag by
 
 // Maximum that propagates NaN (IEEE maximum): gfx950 has it as v_maximum3_f32
@@ -159,13 +158,14 @@ struct StageC {
     static constexpr int value = N;
 };
 
-template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQE_ATTN_WPE, GQE_ATTN_WPE)))
+template <typename T, int D, class Shape>
+__global__ __launch_bounds__(Shape::NW * 64) __attribute__((amdgpu_waves_per_eu(Shape::WPE, Shape::WPE)))
 void attn_fwd_kernel(AttnArgs a) {
+    constexpr int NW = Shape::NW;
     constexpr int NT = NW * 64;
     constexpr int QB = kAttnQW / 16;           // 16-query blocks per wave
-    constexpr int BQ = NW * kAttnQW;
-    constexpr int BKV = kAttnBKV;
+    constexpr int BQ = Shape::BQ;
+    constexpr int BKV = Shape::BKV;
     constexpr int KB = BKV / 16;               // 16-key blocks per tile
     constexpr int KC = BKV / 32;               // 32-key steps of the second product
     constexpr int ES = sizeof(T);

@@ -41,11 +41,9 @@ using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
 using GrpBf16 = TileCfg<bf16, 128, 64, 4, 1>;
 using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
 
-constexpr int kAttnWaves = kAttnNW;             // waves per attention workgroup
-constexpr int kBQ = kAttnWaves * kAttnQW;       // attention query tile
 // Sequence padding of the K / V^T buffers: whole key tiles of the forward
 // and whole key blocks of the dK/dV kernel (its waves read their keys' rows).
-constexpr int kKVPad = kAttnBKV > kBwdBKMax ? kAttnBKV : kBwdBKMax;
+constexpr int kKVPad = std::max({AttnShort::BKV, AttnLong::BKV, kBwdBKMax});
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -232,23 +230,36 @@ void run_grouped_q(const Dims& d, const void* x, const void* Wq, void* Qr, const
     else hipLaunchKernelGGL((grouped_q_kernel<bf16, GrpBf16>), grid, dim3(GrpBf16::NTH), 0, st, g);
 }
 
+// Attention tile shape by sequence length: AttnShort up to T = 256K, AttnLong
+// beyond (measured on the 8-group d = 64 layer: AttnShort 1-3% ahead from
+// T = 64K to 256K, even at 512K, AttnLong 34% ahead at 1M).
+#ifndef GQE_ATTN_LONG_T
+#define GQE_ATTN_LONG_T 262144
+#endif
+constexpr int64_t kAttnLongT = GQE_ATTN_LONG_T;
+template <class Shape>
+void launch_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
+    const bool xcls = a.Q1 != nullptr;
+    a.n_o = (int)((d.T * a.R + Shape::BQ - 1) / Shape::BQ);
+    a.n_x = xcls ? (int)((d.T * (a.R + 1) + Shape::BQ - 1) / Shape::BQ) : 0;
+    const int64_t n_wg = d.B * ((int64_t)(xcls ? d.G - 1 : d.G) * a.n_o + a.n_x);
+    const dim3 grid((unsigned)n_wg), block(Shape::NW * 64);
+    if (d.f32) {
+        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64, Shape>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_fwd_kernel<float, 32, Shape>), grid, block, 0, st, a);
+    } else {
+        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64, Shape>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_fwd_kernel<bf16, 32, Shape>), grid, block, 0, st, a);
+    }
+}
+
 void run_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
     a.T = d.T;
     a.Tpad = d.Tpad;
     a.Bt = (int)d.B;
-    const bool xcls = a.Q1 != nullptr;
-    a.n_o = (int)((d.T * a.R + kBQ - 1) / kBQ);
-    a.n_x = xcls ? (int)((d.T * (a.R + 1) + kBQ - 1) / kBQ) : 0;
     a.G = d.G;
-    const int64_t n_wg = d.B * ((int64_t)(xcls ? d.G - 1 : d.G) * a.n_o + a.n_x);
-    const dim3 grid((unsigned)n_wg), block(kAttnWaves * 64);
-    if (d.f32) {
-        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64, kAttnWaves>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((attn_fwd_kernel<float, 32, kAttnWaves>), grid, block, 0, st, a);
-    } else {
-        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64, kAttnWaves>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((attn_fwd_kernel<bf16, 32, kAttnWaves>), grid, block, 0, st, a);
-    }
+    if (d.T > kAttnLongT) launch_attention<AttnLong>(d, a, st);
+    else launch_attention<AttnShort>(d, a, st);
 }
 
 // The merge step of the variant: the renormalised weighted slot (full,
