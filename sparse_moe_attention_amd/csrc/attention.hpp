@@ -66,8 +66,8 @@ __device__ __forceinline__ int64_t attn_lse_base(const AttnArgs& a, int g, int b
     return before + (int64_t)b * (xg ? a.lse_Lx : a.lse_Lr);
 }
 
-// Tile shapes: queries per wave (both), then waves per workgroup, keys per
-// tile and the waves per SIMD the register budget is sized for.
+// Tile shapes: queries per wave, waves per workgroup, keys per tile and the
+// waves per SIMD the register budget is sized for.
 //   * Short sequences: four-wave workgroups of 128 query rows with 64-key
 //     tiles (32 KB of LDS for the two stages), three workgroups per CU. The
 //     waves that share a SIMD then belong to different workgroups, whose
@@ -81,13 +81,15 @@ __device__ __forceinline__ int64_t attn_lse_base(const AttnArgs& a, int g, int b
 //     caches (T = 1M: 256 MB per group) 128-row tiles are held near
 //     128 flop/byte x 8 TB/s = 1 PFLOP/s by HBM; 256-row tiles halve those
 //     reads (T = 1M: 1.10 s against 1.48 s per layer).
-constexpr int kAttnQW = 32;
-template <int NW_, int BKV_, int WPE_>
+template <int QW_, int NW_, int BKV_, int WPE_>
 struct AttnShape {
-    static constexpr int NW = NW_, BKV = BKV_, WPE = WPE_, BQ = NW_ * kAttnQW;
+    static constexpr int QW = QW_, NW = NW_, BKV = BKV_, WPE = WPE_, BQ = NW_ * QW_;
 };
-using AttnShort = AttnShape<4, 64, 3>;
-using AttnLong = AttnShape<8, 128, 2>;
+#ifndef GQE_ATTN_SHORT_SHAPE
+#define GQE_ATTN_SHORT_SHAPE 32, 4, 64, 3
+#endif
+using AttnShort = AttnShape<GQE_ATTN_SHORT_SHAPE>;
+using AttnLong = AttnShape<32, 8, 128, 2>;
 constexpr float kLazyRescale = 8.f;   // log2 units the running max may lag by
 
 // Maximum that propagates NaN (IEEE maximum): gfx950 has it as v_maximum3_f32
@@ -161,9 +163,9 @@ struct StageC {
 template <typename T, int D, class Shape>
 __global__ __launch_bounds__(Shape::NW * 64) __attribute__((amdgpu_waves_per_eu(Shape::WPE, Shape::WPE)))
 void attn_fwd_kernel(AttnArgs a) {
-    constexpr int NW = Shape::NW;
+    constexpr int NW = Shape::NW, QW = Shape::QW;
     constexpr int NT = NW * 64;
-    constexpr int QB = kAttnQW / 16;           // 16-query blocks per wave
+    constexpr int QB = QW / 16;           // 16-query blocks per wave
     constexpr int BQ = Shape::BQ;
     constexpr int BKV = Shape::BKV;
     constexpr int KB = BKV / 16;               // 16-key blocks per tile
@@ -233,13 +235,13 @@ void attn_fwd_kernel(AttnArgs a) {
     const int64_t vrow = (int64_t)a.Bt * a.Tpad;
     const T* Vg = (const T*)a.Vt + (int64_t)g * D * vrow + (int64_t)b * a.Tpad;
     const int64_t tok0 = (int64_t)b * T_;
-    const int row0 = qt * BQ + wave * kAttnQW;           // first row of this wave
+    const int row0 = qt * BQ + wave * QW;           // first row of this wave
     // Token of each row this lane holds (query column l16 of block qb).
     int tq[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) tq[qb] = (row0 + qb * 16 + l16) / Rg;
     const int t_first = row0 / Rg;                       // tokens spanned by this wave
-    const int t_last = (int)min<int64_t>(T_ - 1, (row0 + kAttnQW - 1) / Rg);
+    const int t_last = (int)min<int64_t>(T_ - 1, (row0 + QW - 1) / Rg);
     // Query and output row pointers of a row (token t, head slot r).
     auto q_row = [&](int t, int r) -> const T* {
         return r < a.R ? (const T*)a.Q0 + (tok0 + t) * a.q0_ld + (int64_t)(g * a.R + r) * D

@@ -39,9 +39,10 @@ template <> __device__ __forceinline__ Frag<float> ld_tile_frag<float>(const cha
     return f;
 }
 
-template <typename T, int BM_, int BN_, int WM_, int WN_>
+template <typename T, int BM_, int BN_, int WM_, int WN_, int WPE_ = 2>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int WPE = WPE_;                    // waves per SIMD the registers are sized for
     static constexpr int BK = 128 / sizeof(T);          // K elements per 128-byte row
     static constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
     static constexpr int FM = BM / (16 * WM);           // 16x16 blocks per wave, rows
@@ -259,7 +260,10 @@ __device__ __forceinline__ void gemm_kloop(char* lds0, char* lds1, const T* cons
 // Each tile then writes straight from the accumulators, oriented so that a
 // lane's four consecutive values run along the output's contiguous axis.
 // ---------------------------------------------------------------------------
-constexpr int kProjClassAlign = 128;
+#ifndef GQE_PROJ_ALIGN
+#define GQE_PROJ_ALIGN 128
+#endif
+constexpr int kProjClassAlign = GQE_PROJ_ALIGN;
 
 // Four consecutive outputs from an accumulator, scaled (8 bytes bf16, 16
 // fp32), as a non-temporal store: projection outputs are read by a later
@@ -515,7 +519,7 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* l
 // multiple of 8, so every tile index keeps its XCD), which lets one tile's
 // stores drain while the next tile's K loop runs.
 template <typename T, class Cfg>
-__global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_gemm_kernel(ProjArgs a) {
+__global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(Cfg::WPE, Cfg::WPE))) void proj_gemm_kernel(ProjArgs a) {
     // Two LDS stages; with the register-staged K loop they must be contiguous.
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     __shared__ __attribute__((aligned(16))) char lds_b[GQE_GEMM_DMA ? Cfg::STAGE_BYTES : 16];

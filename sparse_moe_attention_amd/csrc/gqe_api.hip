@@ -32,11 +32,10 @@ using namespace gqe;
 
 namespace {
 
-#ifndef GQE_PROJ_BM
-#define GQE_PROJ_BM 128
-#define GQE_PROJ_WM 2
+#ifndef GQE_PROJ_CFG
+#define GQE_PROJ_CFG 128, 128, 2, 2, 2
 #endif
-using ProjBf16 = TileCfg<bf16, GQE_PROJ_BM, 128, GQE_PROJ_WM, 2>;
+using ProjBf16 = TileCfg<bf16, GQE_PROJ_CFG>;
 using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
 using GrpBf16 = TileCfg<bf16, 128, 64, 4, 1>;
 using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
@@ -137,7 +136,7 @@ void launch_proj(ProjArgs& a, int total_cols, hipStream_t st) {
     // Eight resident waves per CU (two per SIMD: the register budget), in
     // whole XCD rounds.
     const int64_t tiles = n_m * a.n_tiles_n * (a.n_split > 1 ? a.n_split : 1);
-    const int per_cu = 8 / (Cfg::WM * Cfg::WN);
+    const int per_cu = std::max(1, Cfg::WPE * 4 / (Cfg::WM * Cfg::WN));
     const int64_t grid = std::min<int64_t>(tiles, per_cu * (int64_t)align_up((size_t)device_cus(), 8));
     hipLaunchKernelGGL((proj_gemm_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NTH), 0, st, a);
 }
