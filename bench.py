@@ -208,12 +208,12 @@ def cpu_baseline(s, inp, target_s: float):
     # calibrate the row count on a small sample, then fill the time budget
     r0 = 16
     t = time.perf_counter()
-    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, sample_rows(s, r0, 7), variant=s.variant)
+    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, sample_rows(s, r0, 7), shared_kv_group=s.shared_kv_group, variant=s.variant)
     per_row = max((time.perf_counter() - t - t_fixed) / r0, 1e-6)
     R = int(min(s.N, max(r0, (target_s - t_fixed) / per_row)))
     rows = sample_rows(s, R, 11)
     t = time.perf_counter()
-    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, rows, variant=s.variant)
+    go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, rows, shared_kv_group=s.shared_kv_group, variant=s.variant)
     t_rows = time.perf_counter() - t
     per_row = max((t_rows - t_fixed) / len(rows), 1e-9)
     est = t_fixed + s.N * per_row

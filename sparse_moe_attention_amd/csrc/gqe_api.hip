@@ -231,25 +231,21 @@ void run_grouped_q(const Dims& d, const void* x, const void* Wq, void* Qr, const
 
 // Attention tile shape by sequence length: AttnShort up to T = 256K, AttnLong
 // beyond (measured on the 8-group d = 64 layer: AttnShort 1-3% ahead from
-// T = 64K to 256K, even at 512K, AttnLong 34% ahead at 1M).
+// T = 64K to 256K, even at 512K, AttnLong 34% ahead at 1M). fp32 layers (the
+// small reference configuration) always take AttnShort.
 #ifndef GQE_ATTN_LONG_T
 #define GQE_ATTN_LONG_T 262144
 #endif
 constexpr int64_t kAttnLongT = GQE_ATTN_LONG_T;
-template <class Shape>
+template <typename T, class Shape>
 void launch_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
     const bool xcls = a.Q1 != nullptr;
     a.n_o = (int)((d.T * a.R + Shape::BQ - 1) / Shape::BQ);
     a.n_x = xcls ? (int)((d.T * (a.R + 1) + Shape::BQ - 1) / Shape::BQ) : 0;
     const int64_t n_wg = d.B * ((int64_t)(xcls ? d.G - 1 : d.G) * a.n_o + a.n_x);
     const dim3 grid((unsigned)n_wg), block(Shape::NW * 64);
-    if (d.f32) {
-        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<float, 64, Shape>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((attn_fwd_kernel<float, 32, Shape>), grid, block, 0, st, a);
-    } else {
-        if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<bf16, 64, Shape>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((attn_fwd_kernel<bf16, 32, Shape>), grid, block, 0, st, a);
-    }
+    if (d.d == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64, Shape>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, 32, Shape>), grid, block, 0, st, a);
 }
 
 void run_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
@@ -257,8 +253,9 @@ void run_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
     a.Tpad = d.Tpad;
     a.Bt = (int)d.B;
     a.G = d.G;
-    if (d.T > kAttnLongT) launch_attention<AttnLong>(d, a, st);
-    else launch_attention<AttnShort>(d, a, st);
+    if (d.f32) launch_attention<float, AttnShort>(d, a, st);
+    else if (d.T > kAttnLongT) launch_attention<bf16, AttnLong>(d, a, st);
+    else launch_attention<bf16, AttnShort>(d, a, st);
 }
 
 // The merge step of the variant: the renormalised weighted slot (full,

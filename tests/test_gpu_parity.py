@@ -213,3 +213,47 @@ def test_config_sampled_parity(cid, n_rows):
         torch.cuda.synchronize()
         err, bound = H.out_error(H.np32(og[torch.from_numpy(rows).cuda()]), gref["out"])
         assert err <= bound, ("gqa", err, bound)
+
+
+# Sequences past 256K tokens take the long-context attention tile shape
+# (8 waves x 32 rows, 128-key tiles); the 1M-token workload above covers it at
+# d = 64 with T a multiple of the tile. These add a ragged T (a partial last
+# key tile and row tile), d = 32, k = 2 with the shared head on group 1, two
+# sequences, and the dense GQA layer, on sampled rows that include the last
+# rows of each sequence.
+LONG_CASES = {
+    "long_ragged_d32_k2": Shape(B=2, T=262144 + 1037, D=64, G=2, M=3, k=2, d=32, router_bias=True,
+                                shared_kv_group=1),
+    "long_ragged_d64": Shape(B=1, T=262144 + 4099, D=64, G=3, M=2, k=1, d=64),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", sorted(LONG_CASES))
+def test_long_shape_sampled_parity(name):
+    s = LONG_CASES[name]
+    print(f"[long case {name}] {s}", flush=True)
+    inp = make_inputs(s, seed=77 + len(name))
+    f = H.f64_inputs(inp)
+    dv = H.to_device(inp)
+    del inp
+    idx, w, (lref, sref, wref), near, bad = check_routing(s, f, dv, name)
+    tails = [b * s.T + t for b in range(s.B) for t in (s.T - 1, s.T - 2, s.T - 129, s.T - 1037)]
+    rows = np.unique(np.concatenate([sample_rows(s, 48, seed=2000 + len(name)), np.array(tails, dtype=np.int64)]))
+    ref = go.gqe_rows(f, s.G, s.M, s.k, s.d, s.B, s.T, rows, shared_kv_group=s.shared_kv_group)
+    o = H.alloc_outputs(s)
+    H.run_gqe(s, dv, o)
+    torch.cuda.synchronize()
+    got = H.np32(o["out"][torch.from_numpy(rows).cuda()])
+    keep = ~bad[rows]
+    err, bound = H.out_error(got[keep], ref["out"][keep])
+    print(f"[long case {name}] sampled out max err {err:.3e} bound {bound:.3e}; mismatched {int(bad.sum())}",
+          flush=True)
+    assert np.isfinite(got).all() and err <= bound
+    gref = go.gqa_rows(dict(x=f["x"], Wq=f["Wq"], Wk=f["Wk"], Wv=f["Wv"], Wo=f["Wo_gqa"]),
+                       s.G, s.Hq, s.d, s.B, s.T, rows)
+    og = torch.empty_like(o["out"])
+    H.run_gqa(s, dv, og)
+    torch.cuda.synchronize()
+    err, bound = H.out_error(H.np32(og[torch.from_numpy(rows).cuda()]), gref["out"])
+    assert err <= bound, ("gqa", err, bound)
