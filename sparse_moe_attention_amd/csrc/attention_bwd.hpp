@@ -59,7 +59,12 @@ struct AttnBwdArgs {
 
 // Tile shapes (the dK/dV kernel: keys per wave, waves, query rows per
 // sub-step, waves per SIMD the registers are sized for; the dQ kernel: rows
-// per wave, waves, keys per sub-step).
+// per wave, waves, keys per sub-step, waves per SIMD, keys per staged tile).
+// The dQ kernel runs three four-wave workgroups per CU (64-key tiles keep
+// their LDS at 48 KB, 32-key sub-steps their registers at 168): the waves
+// sharing a SIMD then come from independent workgroups and overlap one
+// another's exponent and product phases (10% faster than one eight-wave
+// workgroup of 128-key tiles per CU at T = 32K).
 #ifndef GQE_BWD_KW
 #define GQE_BWD_KW 32
 #endif
@@ -76,13 +81,16 @@ struct AttnBwdArgs {
 #define GQE_BWD_DQ_QW 32
 #endif
 #ifndef GQE_BWD_DQ_NW
-#define GQE_BWD_DQ_NW 8
+#define GQE_BWD_DQ_NW 4
 #endif
 #ifndef GQE_BWD_DQ_KS
-#define GQE_BWD_DQ_KS 64
+#define GQE_BWD_DQ_KS 32
 #endif
 #ifndef GQE_BWD_DQ_WPE
-#define GQE_BWD_DQ_WPE 2
+#define GQE_BWD_DQ_WPE 3
+#endif
+#ifndef GQE_BWD_DQ_BKV
+#define GQE_BWD_DQ_BKV 64
 #endif
 constexpr int kBwdKW = GQE_BWD_KW;         // keys per wave (dK/dV kernel)
 // Waves per dK/dV workgroup: head width 32 stages half the bytes per step,
@@ -95,7 +103,7 @@ constexpr int kBwdRS = GQE_BWD_RS;         // rows per sub-step
 constexpr int kBwdDqQW = GQE_BWD_DQ_QW;    // rows per wave (dQ kernel)
 constexpr int kBwdDqNW = GQE_BWD_DQ_NW;    // waves per dQ workgroup
 constexpr int kBwdDqBQ = kBwdDqNW * kBwdDqQW;
-constexpr int kBwdBKV = 128;               // keys per staged tile (dQ kernel)
+constexpr int kBwdBKV = GQE_BWD_DQ_BKV;    // keys per staged tile (dQ kernel)
 constexpr int kBwdDqKS = GQE_BWD_DQ_KS;    // keys per sub-step
 static_assert(kBwdKW % 16 == 0 && kBwdQB % kBwdRS == 0 && kBwdRS % 32 == 0, "dK/dV tile shape");
 static_assert(kBwdDqQW % 16 == 0 && kBwdBKV % kBwdDqKS == 0 && kBwdDqKS % 32 == 0, "dQ tile shape");
