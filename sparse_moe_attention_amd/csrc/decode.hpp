@@ -137,10 +137,7 @@ template <int D>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(GQE_DEC_WPE)))
 void attn_decode_kernel(DecodeArgs a) {
     constexpr int DK = D / 32, CB = D / 16;
-#ifndef GQE_DEC_KS
-#define GQE_DEC_KS 64
-#endif
-    constexpr int KS = GQE_DEC_KS;                  // keys per step
+    constexpr int KS = 64;                          // keys per step
     constexpr int KB = KS / 16, KH = KS / 32;       // 16-key score blocks, 32-key product steps
     constexpr int NB = kDecCW / KS;                 // steps per wave
     const int tid = threadIdx.x, lane = tid & 63;
@@ -257,10 +254,6 @@ void attn_decode_kernel(DecodeArgs a) {
                 for (int cb = 0; cb < CB; ++cb) o[cb] = mma16(vf[h][cb], pf, o[cb]);
             }
         };
-#ifndef GQE_DEC_DB
-#define GQE_DEC_DB 1
-#endif
-#if GQE_DEC_DB
         // Two register sets: the next step's loads are in flight during this step's products.
         if (nb > 0) load(0, kA, vA);
         for (int j = 0; j < nb; j += 2) {
@@ -271,12 +264,6 @@ void attn_decode_kernel(DecodeArgs a) {
                 compute(j + 1, kB, vB);
             }
         }
-#else
-        for (int j = 0; j < nb; ++j) {
-            load(j, kA, vA);
-            compute(j, kA, vA);
-        }
-#endif
         // Merge the waves: lane (l16, q4) holds head l16, columns 16cb + 4*q4 + v.
         const float l = __shfl(lsum[0], l16);
         if (q4 == 0) {

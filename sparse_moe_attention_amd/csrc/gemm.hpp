@@ -13,11 +13,6 @@
 
 #include "gqe_common.hpp"
 
-// 1: K loops stage tiles with direct global->LDS loads; 0: through registers.
-#ifndef GQE_GEMM_DMA
-#define GQE_GEMM_DMA 1
-#endif
-
 namespace gqe {
 
 // LDS tile rows are 128 bytes (one K step), unpadded; the eight 16-byte
@@ -54,115 +49,27 @@ struct TileCfg {
     static constexpr int A_BYTES = BM * kPitch;
     static constexpr int B_BYTES = BN * kPitch;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = (GQE_GEMM_DMA ? 1 : 2) * STAGE_BYTES;   // the second DMA stage is its own array
+    static constexpr int LDS_BYTES = STAGE_BYTES;       // one stage; the second is an array of its own
     static_assert(WM * WN == 4 || WM * WN == 8, "4 or 8 waves");
     static_assert(BM * 8 % NTH == 0 && BN * 8 % NTH == 0, "tile rows must split over the threads");
 };
 
 // K loop. a_row[i] / b_row[i] point at the tile rows this thread loads
-// (row tid/8 + 32*i), already offset by its 16-byte column chunk. Every
+// (row tid/8 + RPP*i), already offset by its 16-byte column chunk. Every
 // pointer must be readable for the whole K range: rows outside the problem
 // point at some valid row instead (their results are never stored), so the
-// loads need no branches. Chunks at or beyond K (only in a partial last step)
-// read A as zero and B from the row's first chunk, so they add nothing.
-// Global loads run two K steps ahead of the MFMAs (two register sets), LDS
-// holds two steps. Leaves the C block of this wave in acc and the LDS free
-// (all waves past the final barrier). In 16x16 block (i, j) of the wave a
-// lane holds 4 consecutive entries along one line of C: without SWAP, rows
-// 4*(lane/16) .. +3 of column lane%16 (acc = A-block x B-block^T); with SWAP
-// the transposed block, i.e. columns 4*(lane/16) .. +3 of row lane%16.
-template <typename T, class Cfg, bool SWAP>
-__device__ __forceinline__ void gemm_mainloop(char* lds, const T* const (&a_row)[Cfg::A_PER_THREAD],
-                                              const T* const (&b_row)[Cfg::B_PER_THREAD], int K,
-                                              f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
-    const int c16 = tid & 7;
-    const int nk = (K + Cfg::BK - 1) / Cfg::BK;
-    u32x4 ra0[Cfg::A_PER_THREAD], rb0[Cfg::B_PER_THREAD];
-    u32x4 ra1[Cfg::A_PER_THREAD], rb1[Cfg::B_PER_THREAD];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto gload = [&](int kt, u32x4 (&ra)[Cfg::A_PER_THREAD], u32x4 (&rb)[Cfg::B_PER_THREAD]) {
-        if ((kt + 1) * Cfg::BK <= K) {        // whole step inside K
-#pragma unroll
-            for (int i = 0; i < Cfg::A_PER_THREAD; ++i) ra[i] = ld16(a_row[i] + kt * Cfg::BK);
-#pragma unroll
-            for (int i = 0; i < Cfg::B_PER_THREAD; ++i) rb[i] = ld16(b_row[i] + kt * Cfg::BK);
-        } else {
-            const bool kin = kt * Cfg::BK + c16 * Cfg::VEC < K;
-            const int ko = kin ? kt * Cfg::BK : 0;
-#pragma unroll
-            for (int i = 0; i < Cfg::A_PER_THREAD; ++i) {
-                const u32x4 v = ld16(a_row[i] + ko);
-                ra[i] = kin ? v : zero;
-            }
-#pragma unroll
-            for (int i = 0; i < Cfg::B_PER_THREAD; ++i) rb[i] = ld16(b_row[i] + ko);
-        }
-    };
-    auto sstore = [&](int buf, const u32x4 (&ra)[Cfg::A_PER_THREAD], const u32x4 (&rb)[Cfg::B_PER_THREAD]) {
-        char* As = lds + buf * Cfg::STAGE_BYTES;
-        char* Bs = As + Cfg::A_BYTES;
-#pragma unroll
-        for (int i = 0; i < Cfg::A_PER_THREAD; ++i) st16(As + tile_off(tid / 8 + Cfg::RPP * i, c16), ra[i]);
-#pragma unroll
-        for (int i = 0; i < Cfg::B_PER_THREAD; ++i) st16(Bs + tile_off(tid / 8 + Cfg::RPP * i, c16), rb[i]);
-    };
-    auto compute = [&](int buf) {
-        const char* As = lds + buf * Cfg::STAGE_BYTES;
-        const char* Bs = As + Cfg::A_BYTES;
-#pragma unroll
-        for (int ks = 0; ks < Cfg::BK / 32; ++ks) {
-            const int kc = (ks * 32 + 8 * (lane >> 4)) * (int)sizeof(T) / 16;   // 16-byte chunk
-            Frag<T> af[Cfg::FM], bfg[Cfg::FN];
-#pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
-                af[i] = ld_tile_frag<T>(As, (wm * Cfg::FM + i) * 16 + (lane & 15), kc);
-#pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j)
-                bfg[j] = ld_tile_frag<T>(Bs, (wn * Cfg::FN + j) * 16 + (lane & 15), kc);
-#pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j)
-                    acc[i][j] = SWAP ? mma16(bfg[j], af[i], acc[i][j]) : mma16(af[i], bfg[j], acc[i][j]);
-        }
-    };
-    // Step kt computes from LDS buffer kt%2, refills the register set that
-    // held step kt with step kt+2, and moves step kt+1 (loaded one step ago)
-    // from the other register set into LDS buffer (kt+1)%2.
-    auto step = [&](int kt, u32x4 (&ra_kt)[Cfg::A_PER_THREAD], u32x4 (&rb_kt)[Cfg::B_PER_THREAD],
-                    const u32x4 (&ra_n)[Cfg::A_PER_THREAD], const u32x4 (&rb_n)[Cfg::B_PER_THREAD]) {
-        if (kt + 2 < nk) gload(kt + 2, ra_kt, rb_kt);
-        compute(kt & 1);
-        if (kt + 1 < nk) sstore((kt + 1) & 1, ra_n, rb_n);
-        __syncthreads();
-    };
-
-    gload(0, ra0, rb0);
-    if (nk > 1) gload(1, ra1, rb1);
-    sstore(0, ra0, rb0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, ra0, rb0, ra1, rb1);
-        if (kt + 1 < nk) step(kt + 1, ra1, rb1, ra0, rb0);
-    }
-}
-
-// The same K loop with the tiles staged by gfx950's direct global->LDS loads
-// (global_load_lds_dwordx4): each lane fetches the global chunk that the
+// loads need no branches. Tiles are staged with gfx950's direct global->LDS
+// loads (global_load_lds_dwordx4): each lane fetches the global chunk that the
 // swizzled layout puts in its LDS slot, so tiles never pass through
 // registers. Stage kt+1 loads while stage kt computes; the two stages are
 // separate LDS arrays, so the compiler does not make the reads of one wait
 // for the loads into the other. A partial last K step zeroes the A chunks at
 // or beyond K in LDS (their B chunks hold finite data from the row start).
+// Leaves the C block of this wave in acc and the LDS free (all waves past the
+// final barrier). In 16x16 block (i, j) of the wave a lane holds 4
+// consecutive entries along one line of C: without SWAP, rows 4*(lane/16) ..
+// +3 of column lane%16 (acc = A-block x B-block^T); with SWAP the transposed
+// block, i.e. columns 4*(lane/16) .. +3 of row lane%16.
 template <typename T, class Cfg, bool SWAP>
 __device__ __forceinline__ void gemm_mainloop_dma(char* lds0, char* lds1, const T* const (&a_row)[Cfg::A_PER_THREAD],
                                                   const T* const (&b_row)[Cfg::B_PER_THREAD], int K,
@@ -238,17 +145,12 @@ __device__ __forceinline__ void gemm_mainloop_dma(char* lds0, char* lds1, const 
     }
 }
 
-// Dispatch to the configured K loop; lds0/lds1 are two STAGE_BYTES arrays.
+// The K loop over two STAGE_BYTES arrays.
 template <typename T, class Cfg, bool SWAP>
 __device__ __forceinline__ void gemm_kloop(char* lds0, char* lds1, const T* const (&a_row)[Cfg::A_PER_THREAD],
                                            const T* const (&b_row)[Cfg::B_PER_THREAD], int K,
                                            f32x4 (&acc)[Cfg::FM][Cfg::FN]) {
-    if constexpr (GQE_GEMM_DMA) {
-        gemm_mainloop_dma<T, Cfg, SWAP>(lds0, lds1, a_row, b_row, K, acc);
-    } else {
-        static_assert(Cfg::STAGE_BYTES % 16 == 0, "stages are contiguous");
-        gemm_mainloop<T, Cfg, SWAP>(lds0, a_row, b_row, K, acc);   // uses lds0[0, 2*STAGE_BYTES)
-    }
+    gemm_mainloop_dma<T, Cfg, SWAP>(lds0, lds1, a_row, b_row, K, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -520,10 +422,10 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, char* lds0, char* l
 // stores drain while the next tile's K loop runs.
 template <typename T, class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(Cfg::WPE, Cfg::WPE))) void proj_gemm_kernel(ProjArgs a) {
-    // Two LDS stages; with the register-staged K loop they must be contiguous.
+    // Two LDS stages, as separate arrays.
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds_b[GQE_GEMM_DMA ? Cfg::STAGE_BYTES : 16];
-    char* lds1 = GQE_GEMM_DMA ? lds_b : lds + Cfg::STAGE_BYTES;
+    __shared__ __attribute__((aligned(16))) char lds_b[Cfg::STAGE_BYTES];
+    char* lds1 = lds_b;
     const int64_t n = ((a.M_rows + Cfg::BM - 1) / Cfg::BM) * a.n_tiles_n * (a.n_split > 1 ? a.n_split : 1);
     for (int64_t hw = blockIdx.x; hw < n; hw += gridDim.x) proj_tile<T, Cfg>(a, lds, lds1, hw);
 }
@@ -645,8 +547,8 @@ struct GroupArgs {
 template <typename T, class Cfg>
 __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_q_kernel(GroupArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds_b[GQE_GEMM_DMA ? Cfg::STAGE_BYTES : 16];
-    char* lds1 = GQE_GEMM_DMA ? lds_b : lds + Cfg::STAGE_BYTES;
+    __shared__ __attribute__((aligned(16))) char lds_b[Cfg::STAGE_BYTES];
+    char* lds1 = lds_b;
     __shared__ int32_t s_dst[Cfg::BM];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
