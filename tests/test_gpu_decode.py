@@ -134,3 +134,42 @@ def test_decode_parity_at_bench_workload():
         err, bound = H.out_error(H.np32(vtd.view(s.G, s.d, B, T)[:, :, b, T - 1]), ref["V_new"][i])
         assert err <= bound, ("appended value", b, err, bound)
     assert torch.isfinite(out.float()).all()
+
+
+def test_decode_positions_out_of_range():
+    """Entries of pos outside [0, T) are documented to leave their sequence's
+    cache untouched (no read, no write, outputs unspecified); the other
+    sequences of the same call still match the oracle."""
+    s = Shape(B=4, T=128, D=64, G=2, M=2, k=1, d=32, shared_kv_group=1)
+    pos = [17, -1, 128, 127]
+    valid = [0, 3]
+    print(f"[decode out-of-range positions] {s} pos={pos}", flush=True)
+    inp = make_inputs(Shape(B=s.B, T=1, D=s.D, G=s.G, M=s.M, k=s.k, d=s.d, shared_kv_group=s.shared_kv_group),
+                      seed=901)
+    kc, vc, vtc = make_caches(s, [p if 0 <= p < s.T else s.T for p in pos], seed=902)
+    dv = H.to_device(inp)
+    kd, vtd = kc.cuda(), vtc.cuda()
+    posd = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    sh = gq.shape_from(s)
+    ws = torch.empty(gq.gqe_decode_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    out = torch.empty(s.B, s.D, dtype=torch.bfloat16, device="cuda")
+    gq.gqe_decode_step(sh, posd, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"], dv["Wo"],
+                       kd, vtd, out, ws)
+    torch.cuda.synchronize()
+    f = H.f64_inputs(inp)
+    f_sel = dict(f, x=f["x"][valid])
+    k64 = kc[:, valid].float().numpy().astype(np.float64).transpose(1, 0, 2, 3)
+    v64 = vc[:, valid].float().numpy().astype(np.float64).transpose(1, 0, 2, 3)
+    ref = gd.gqe_decode(f_sel, k64, v64, [pos[b] for b in valid], s.G, s.M, s.k, s.d,
+                        shared_kv_group=s.shared_kv_group)
+    got = H.np32(out)[valid]
+    err, bound = H.out_error(got, ref["out"])
+    assert np.isfinite(got).all() and err <= bound, ("out", err, bound)
+    # the caches of the out-of-range sequences are bit-identical
+    k_after = kd.cpu()
+    v_after = vtd.cpu().reshape(s.G, s.d, s.B, s.T)
+    v_before = vtc.reshape(s.G, s.d, s.B, s.T)
+    for b in (1, 2):
+        assert torch.equal(k_after[:, b].view(torch.int16), kc[:, b].view(torch.int16)), ("key cache written", b)
+        assert torch.equal(v_after[:, :, b].contiguous().view(torch.int16),
+                           v_before[:, :, b].contiguous().view(torch.int16)), ("value cache written", b)
