@@ -42,6 +42,8 @@ CASES = {
     "one_expert": (Shape(B=1, T=130, D=64, G=4, M=1, k=1, d=32), 0.1),
     "all_experts": (Shape(B=2, T=150, D=128, G=2, M=3, k=3, d=64), 0.0),
     "wide_pool": (Shape(B=1, T=260, D=128, G=4, M=16, k=4, d=32, router_bias=True), 0.03),
+    "max_pool_256_experts": (Shape(B=2, T=131, D=64, G=4, M=64, k=3, d=32, router_bias=True, shared_kv_group=3),
+                             0.02),
     "long": (Shape(B=1, T=2048, D=512, G=4, M=2, k=1, d=64), 0.01),
 }
 

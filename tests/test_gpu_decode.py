@@ -31,6 +31,8 @@ CASES = {
     "short": (Shape(B=4, T=64, D=64, G=2, M=2, k=1, d=64), [5, 0, 63, 31]),
     "wide_pool": (Shape(B=2, T=1088, D=128, G=4, M=16, k=4, d=32, router_bias=True), [1087, 1024]),
     "seventeen_heads": (Shape(B=2, T=320, D=64, G=2, M=20, k=16, d=32), [300, 17]),
+    "max_pool_256_experts": (Shape(B=2, T=192, D=64, G=4, M=64, k=3, d=32, router_bias=True, shared_kv_group=3),
+                             [100, 191]),
 }
 
 
