@@ -44,6 +44,7 @@ CASES = {
     "wide_pool": (Shape(B=1, T=260, D=128, G=4, M=16, k=4, d=32, router_bias=True), 0.03),
     "max_pool_256_experts": (Shape(B=2, T=131, D=64, G=4, M=64, k=3, d=32, router_bias=True, shared_kv_group=3),
                              0.02),
+    "many_short_sequences": (Shape(B=33, T=37, D=64, G=2, M=2, k=1, d=64), 0.01),
     "long": (Shape(B=1, T=2048, D=512, G=4, M=2, k=1, d=64), 0.01),
 }
 

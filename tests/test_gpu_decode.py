@@ -33,6 +33,7 @@ CASES = {
     "seventeen_heads": (Shape(B=2, T=320, D=64, G=2, M=20, k=16, d=32), [300, 17]),
     "max_pool_256_experts": (Shape(B=2, T=192, D=64, G=4, M=64, k=3, d=32, router_bias=True, shared_kv_group=3),
                              [100, 191]),
+    "many_sequences": (Shape(B=33, T=64, D=64, G=2, M=2, k=1, d=64), [(7 * b) % 64 for b in range(33)]),
 }
 
 

@@ -31,6 +31,7 @@ CASES = {
     "multi_tile": Shape(B=2, T=1000, D=256, G=8, M=2, k=1, d=64),
     "wide_pool": Shape(B=1, T=260, D=128, G=4, M=16, k=4, d=32, router_bias=True),
     "max_pool_256_experts": Shape(B=2, T=131, D=64, G=4, M=64, k=3, d=32, router_bias=True, shared_kv_group=3),
+    "many_short_sequences": Shape(B=33, T=37, D=64, G=2, M=2, k=1, d=64),
     # 9 regular KV streams and one or two shared-head tiles per level: some
     # levels have more streams homed on an XCD than slots landing on it.
     "many_groups": Shape(B=1, T=300, D=128, G=10, M=4, k=4, d=32),
