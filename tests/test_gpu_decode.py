@@ -34,6 +34,9 @@ CASES = {
     "max_pool_256_experts": (Shape(B=2, T=192, D=64, G=4, M=64, k=3, d=32, router_bias=True, shared_kv_group=3),
                              [100, 191]),
     "many_sequences": (Shape(B=33, T=64, D=64, G=2, M=2, k=1, d=64), [(7 * b) % 64 for b in range(33)]),
+    # more than 64 new tokens: the token projections take the tiled GEMM instead of the skinny one
+    "seventy_sequences": (Shape(B=70, T=32, D=64, G=2, M=2, k=1, d=32, shared_kv_group=1),
+                          [(5 * b) % 32 for b in range(70)]),
 }
 
 
