@@ -245,7 +245,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the GQE forward runs on a single MI355X here; "
-              "run it with --gpus 1 (multi-GPU sharding is described in DESIGN.md, not built).",
+              "run it with --gpus 1 (sharding over several GPUs is not built).",
               file=sys.stderr, flush=True)
         sys.exit(2)
 

@@ -17,7 +17,7 @@ float64. Sources (title and section):
            router's learning signal; an auxiliary balancing loss keeps the
            router from always picking the same experts).
 
-Readings (each is listed in DESIGN.md):
+Readings where the pages are silent or garbled:
   * the top-k selection is piecewise constant: no gradient flows through idx;
   * the auxiliary loss is the usual fraction-times-mean-probability form,
     per group and averaged over groups:

@@ -16,7 +16,7 @@ earlier positions:
   O[b,g,r] = softmax_j(q . K[b,g,j] / sqrt(d)) V[b,g,j], j = 0 .. pos[b]
   C = [hard slots | weighted slot | shared slot], out = C Wo^T
 
-Reading (listed in the design doc): the pages describe the cache only as dense and
+Reading where the pages are silent: they describe the cache only as dense and
 unchanged; positions are per sequence (pos[b] cached keys precede the new
 token), and nothing else (no positional encoding) enters the attention.
 """

@@ -19,7 +19,7 @@ float64 with no blocking or fusion beyond what each step states. Sources
   [GQA-w]  aiboss88.com wiki "What is Grouped-Query Attention", section
            "Mechanism" (GQA generalizes MQA; MHA and MQA are its endpoints).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * the router is linear in the token's features, x @ Wr.T, plus an optional
     per-expert offset br; softmax is taken per group over its M experts;
   * top-k orders the experts by descending logit, ties to the lower index;
