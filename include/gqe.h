@@ -66,7 +66,7 @@ typedef enum {
     GQE_OK = 0,
     GQE_ERR_NULL = -1,         /* a required pointer is NULL */
     GQE_ERR_SHAPE = -2,        /* an inconsistent or out-of-range size */
-    GQE_ERR_UNSUPPORTED = -3,  /* a valid size this build does not handle (d_h, D, M, G*M) */
+    GQE_ERR_UNSUPPORTED = -3,  /* a valid size the library does not handle (d_h, D, M, G*M) */
     GQE_ERR_WORKSPACE = -4,    /* ws_bytes smaller than the *_workspace_bytes figure */
     GQE_ERR_ALIGN = -5,        /* a pointer not aligned to 16 bytes */
     GQE_ERR_HIP = -6           /* the HIP runtime reported an error at launch */

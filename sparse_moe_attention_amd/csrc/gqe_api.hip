@@ -1025,7 +1025,7 @@ const char* gqe_status_str(gqe_status st) {
         case GQE_OK: return "GQE_OK: success";
         case GQE_ERR_NULL: return "GQE_ERR_NULL: a required pointer is NULL";
         case GQE_ERR_SHAPE: return "GQE_ERR_SHAPE: inconsistent or out-of-range sizes";
-        case GQE_ERR_UNSUPPORTED: return "GQE_ERR_UNSUPPORTED: sizes this build does not handle";
+        case GQE_ERR_UNSUPPORTED: return "GQE_ERR_UNSUPPORTED: sizes the library does not handle";
         case GQE_ERR_WORKSPACE: return "GQE_ERR_WORKSPACE: workspace smaller than required";
         case GQE_ERR_ALIGN: return "GQE_ERR_ALIGN: a pointer is not 16-byte aligned";
         case GQE_ERR_HIP: return "GQE_ERR_HIP: the HIP runtime reported an error";
