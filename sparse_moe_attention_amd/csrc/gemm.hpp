@@ -545,7 +545,7 @@ struct GroupArgs {
 };
 
 template <typename T, class Cfg>
-__global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_q_kernel(GroupArgs a) {
+__global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(Cfg::WPE, Cfg::WPE))) void grouped_q_kernel(GroupArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     __shared__ __attribute__((aligned(16))) char lds_b[Cfg::STAGE_BYTES];
     char* lds1 = lds_b;

@@ -37,7 +37,16 @@ namespace {
 #endif
 using ProjBf16 = TileCfg<bf16, GQE_PROJ_CFG>;
 using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
-using GrpBf16 = TileCfg<bf16, 128, 64, 4, 1>;
+// The grouped routed-Q GEMM: 128 x 64 tiles (one expert's 64 query columns),
+// three workgroups per CU (its registers fit three waves per SIMD and its two
+// LDS stages take 48 KB): its K steps are short (8 MFMAs per wave), so the
+// extra workgroup hides the tile loads (T = 32K: 72 -> 59 us). The projection
+// GEMM keeps two 128 x 128 workgroups per CU; 128 x 64 or 64 x 128 tiles at
+// three per CU measured slower there (106 -> 121 us).
+#ifndef GQE_GRP_CFG
+#define GQE_GRP_CFG 128, 64, 4, 1, 3
+#endif
+using GrpBf16 = TileCfg<bf16, GQE_GRP_CFG>;
 using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
 
 // Sequence padding of the K / V^T buffers: whole key tiles of the forward
