@@ -80,13 +80,9 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecTokArgs a) {
     __syncthreads();
     if (g == 0 && r == 0 && cb == 0) {
         // The token's routing as route_kernel writes it: the same picks, and
-        // the probabilities renormalised by their sum taken in the same order.
+        // the probabilities renormalised by the same sum (renorm_total).
         const int GK = a.G * a.k;
-        if (tid == 0) {
-            float total = 0.f;
-            for (int q = 0; q < GK; ++q) total += s_p[q];
-            s_inv = 1.f / total;
-        }
+        if (tid == 0) s_inv = 1.f / renorm_total(a.G, a.k, [&](int gg, int rr) { return s_p[gg * a.k + rr]; });
         __syncthreads();
         for (int q = tid; q < GK; q += 256) {
             a.idx[(int64_t)b * GK + q] = s_sel[q];

@@ -209,7 +209,7 @@ void run_proj_rows(const Dims& d, SegList& sl, hipStream_t st) {
 // have their logits loaded into registers at once, others read them one by one.
 void run_route(const Dims& d, const float* lg, int32_t* idx, float* w, int32_t* hist, hipStream_t st) {
     const int renorm = d.variant != GQE_WEIGHTED_CONCAT;
-    const dim3 grid((unsigned)d.nC), blk(256);
+    const dim3 grid((unsigned)d.nC), blk(kRouteThreads);
     switch (d.M) {
         case 1: hipLaunchKernelGGL((route_kernel<0, 1>), grid, blk, 0, st, lg, idx, w, hist, d.N, d.G, d.M, d.k, renorm); break;
         case 2: hipLaunchKernelGGL((route_kernel<0, 2>), grid, blk, 0, st, lg, idx, w, hist, d.N, d.G, d.M, d.k, renorm); break;
@@ -315,7 +315,7 @@ gqe_status run_post_router(const Dims& d, const GqeWs& L, void* ws, const void* 
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, (const int32_t*)at(ws, L.hist), cbase,
                        (int32_t*)at(ws, L.offsets), (int32_t*)nullptr, (int)d.nC, d.E);
     mk.at(3);
-    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)d.nC), dim3(256), 0, st, idx, (const int32_t*)cbase,
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)d.nC), dim3(kRouteThreads), 0, st, idx, (const int32_t*)cbase,
                        (int32_t*)at(ws, L.perm), (int32_t*)at(ws, L.dst), d.N, d.G, d.M, d.k);
     mk.at(4);
     run_grouped_q(d, x, Wq, at(ws, L.Qr), (const int32_t*)at(ws, L.perm), (const int32_t*)at(ws, L.dst),
@@ -873,7 +873,7 @@ gqe_status gqe_attn_fwd_routed(const gqe_shape* s, const void* x, const void* Wq
     const GqeWs L = gqe_layout(d);
     if (ws_bytes < L.total) return GQE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL((route_kernel<1, 0>), dim3((unsigned)d.nC), dim3(256), 0, st, (const float*)nullptr,
+    hipLaunchKernelGGL((route_kernel<1, 0>), dim3((unsigned)d.nC), dim3(kRouteThreads), 0, st, (const float*)nullptr,
                        const_cast<int32_t*>(idx), (float*)nullptr, (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k, 1);
     void* C = slots_out ? slots_out : at(ws, L.C);
     return run_post_router(d, L, ws, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, C, st, true, Marks{nullptr, st});

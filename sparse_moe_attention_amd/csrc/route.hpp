@@ -23,7 +23,7 @@
 
 namespace gqe {
 
-constexpr int kChunk = 256;   // tokens per routing chunk (= workgroup size)
+constexpr int kChunk = 256;   // tokens per routing chunk
 
 // One group of one token: the k best of its M logits (descending, ties to the
 // lower index) and their softmax probabilities over the group, passed to
@@ -63,57 +63,84 @@ __device__ inline void topk_group(const float* zg, int M, int k, Emit&& emit) {
     }
 }
 
-// The routing of one token from its logits row z [G*M]: idx row [G*k] and
-// weights w row [G*k], each written once (a first pass over the groups sums
-// the picks' probabilities for the renormalisation, a second writes); also
-// calls count(e) for every pick's expert e = g*M + m.
-template <int MM, class Count>
-__device__ inline void route_token(const float* z, int G, int M, int k, int renorm, int32_t* irow, float* wrow,
-                                   Count&& count) {
+// Routing works on chunks of kChunk tokens with kRouteQ threads per token:
+// thread (q, t) of a workgroup handles token t of the chunk and the groups
+// [q*GQ, min(G, (q+1)*GQ)), GQ = ceil(G / kRouteQ), so each thread walks a
+// quarter of the groups instead of all of them.
+constexpr int kRouteQ = 4;
+constexpr int kRouteThreads = kRouteQ * kChunk;
+__host__ __device__ inline int route_gq(int G) { return (G + kRouteQ - 1) / kRouteQ; }
+
+// The renormalisation denominator of a token: the picks' probabilities summed
+// group by group (ranks in order) within each quarter of the groups, then the
+// four quarter sums added in order. prob(g, r) returns pick r of group g.
+template <class Prob>
+__device__ inline float renorm_total(int G, int k, Prob&& prob) {
+    const int gq = route_gq(G);
     float total = 0.f;
-    if (renorm)
-        for (int g = 0; g < G; ++g) topk_group<MM>(z + g * M, M, k, [&](int, int, float p) { total += p; });
-    const float inv = renorm ? 1.f / total : 1.f;
-    for (int g = 0; g < G; ++g)
-        topk_group<MM>(z + g * M, M, k, [&](int r, int m, float p) {
-            irow[g * k + r] = m;
-            wrow[g * k + r] = renorm ? p * inv : p;
-            count(g * M + m);
-        });
+    for (int q = 0; q < kRouteQ; ++q) {
+        float part = 0.f;
+        for (int g = q * gq; g < min(G, (q + 1) * gq); ++g)
+            for (int r = 0; r < k; ++r) part += prob(g, r);
+        total += part;
+    }
+    return total;
 }
 
 // MODE 0: route from fp32 logits [N, G*M] -> idx, w and the histogram
 // (renorm = 0: w is the pick's probability, not renormalised). MM as in
-// topk_group.
+// topk_group. The quarter sums of renorm_total meet in LDS, so w is the same
+// value renorm_total gives.
 // MODE 1: histogram of a caller-given idx (entries outside [0, M), and repeats
 // of an earlier rank's expert in the same group, are skipped).
 template <int MODE, int MM>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int32_t* __restrict__ idx,
-                                                    float* __restrict__ w, int32_t* __restrict__ hist, int64_t N,
-                                                    int G, int M, int k, int renorm) {
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits,
+                                                              int32_t* __restrict__ idx, float* __restrict__ w,
+                                                              int32_t* __restrict__ hist, int64_t N, int G, int M,
+                                                              int k, int renorm) {
     __shared__ int32_t h_lds[256];
+    __shared__ float s_part[kRouteQ][kChunk];
     const int E = G * M;
-    for (int e = threadIdx.x; e < E; e += 256) h_lds[e] = 0;
-    __syncthreads();
-    const int64_t n = (int64_t)blockIdx.x * kChunk + threadIdx.x;
+    const int tid = threadIdx.x, q = tid / kChunk, t = tid % kChunk;
+    for (int e = tid; e < E; e += kRouteThreads) h_lds[e] = 0;
+    const int64_t n = (int64_t)blockIdx.x * kChunk + t;
     const int GK = G * k;
-    if (n < N) {
+    const int gq = route_gq(G), g0 = q * gq, g1 = min(G, g0 + gq);
+    const bool valid = n < N;
+    if (MODE == 0) {
+        const float* z = logits + (valid ? n : 0) * E;
+        float part = 0.f;
+        if (valid && renorm)
+            for (int g = g0; g < g1; ++g) topk_group<MM>(z + g * M, M, k, [&](int, int, float p) { part += p; });
+        s_part[q][t] = part;
+    }
+    __syncthreads();
+    if (valid) {
         int32_t* irow = idx + n * GK;
         if (MODE == 0) {
-            route_token<MM>(logits + n * E, G, M, k, renorm, irow, w + n * GK,
-                            [&](int e) { atomicAdd(&h_lds[e], 1); });
+            float* wrow = w + n * GK;
+            float total = 0.f;
+            for (int qq = 0; qq < kRouteQ; ++qq) total += s_part[qq][t];
+            const float inv = renorm ? 1.f / total : 1.f;
+            const float* z = logits + n * E;
+            for (int g = g0; g < g1; ++g)
+                topk_group<MM>(z + g * M, M, k, [&](int r, int m, float p) {
+                    irow[g * k + r] = m;
+                    wrow[g * k + r] = renorm ? p * inv : p;
+                    atomicAdd(&h_lds[g * M + m], 1);
+                });
         } else {
-            for (int g = 0; g < G; ++g)
+            for (int g = g0; g < g1; ++g)
                 for (int r = 0; r < k; ++r) {
                     const int m = irow[g * k + r];
                     bool first = m >= 0 && m < M;          // out-of-range picks are skipped
-                    for (int q = 0; q < r && first; ++q) first = irow[g * k + q] != m;   // so are repeats
+                    for (int qq = 0; qq < r && first; ++qq) first = irow[g * k + qq] != m;   // so are repeats
                     if (first) atomicAdd(&h_lds[g * M + m], 1);
                 }
         }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = h_lds[e];
+    for (int e = tid; e < E; e += kRouteThreads) hist[(int64_t)blockIdx.x * E + e] = h_lds[e];
 }
 
 // One workgroup of 1024 threads. cbase [nC+1][E]: first permutation row of
@@ -166,25 +193,30 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* hist, int32_t
     if (t < E) cbase[(int64_t)nC * E + t] = off[t] + tot[t];
 }
 
-// Workgroup = chunk of 256 tokens, thread = token. For every expert e the
-// picks of the chunk are listed in token order at [cbase[c][e], ...): a
-// token's rank is the number of earlier tokens of its wave that picked e
-// (wave ballot) plus the totals of the earlier waves (one LDS exchange).
-// perm = token, dst = row of the dense [N, G, k] layout (the first rank r at
-// which the token picked e). Two passes over the groups: count, then write;
-// each takes a group's picks as a bit mask over its M experts (picks outside
-// [0, M) are skipped, as route_kernel<1> skips them).
-__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ cbase,
-                                                      int32_t* __restrict__ perm, int32_t* __restrict__ dst, int64_t N,
-                                                      int G, int M, int k) {
-    __shared__ int32_t wtot[4][256];           // picks of expert e in each wave of the chunk
+// Workgroup = chunk of kChunk tokens, kRouteQ threads per token as in
+// route_kernel: waves 4q .. 4q+3 hold the chunk's tokens for the groups of
+// quarter q, so every expert belongs to the waves of one quarter. For every
+// expert e the picks of the chunk are listed in token order at
+// [cbase[c][e], ...): a token's rank is the number of earlier tokens of its
+// wave that picked e (wave ballot) plus the totals of the quarter's earlier
+// waves (one LDS exchange). perm = token, dst = row of the dense [N, G, k]
+// layout (the first rank r at which the token picked e). Two passes over the
+// groups: count, then write; each takes a group's picks as a bit mask over its
+// M experts (picks outside [0, M) are skipped, as route_kernel<1> skips them).
+__global__ __launch_bounds__(kRouteThreads) void scatter_kernel(const int32_t* __restrict__ idx,
+                                                                const int32_t* __restrict__ cbase,
+                                                                int32_t* __restrict__ perm, int32_t* __restrict__ dst,
+                                                                int64_t N, int G, int M, int k) {
+    constexpr int WQ = kChunk / 64;            // waves per quarter
+    __shared__ int32_t wtot[WQ][256];          // picks of expert e in each wave of its quarter
     __shared__ int32_t base[256];              // this chunk's first permutation row of each expert
     const int E = G * M;
-    const int tid = threadIdx.x, wave = tid >> 6;
-    for (int e = tid; e < E; e += 256) base[e] = cbase[(int64_t)blockIdx.x * E + e];
-    const int64_t n = (int64_t)blockIdx.x * kChunk + tid;
+    const int tid = threadIdx.x, q = tid / kChunk, t = tid % kChunk, wq = t >> 6;
+    for (int e = tid; e < E; e += kRouteThreads) base[e] = cbase[(int64_t)blockIdx.x * E + e];
+    const int64_t n = (int64_t)blockIdx.x * kChunk + t;
     const bool valid = n < N;
     const int GK = G * k;
+    const int gq = route_gq(G), g0 = q * gq, g1 = min(G, g0 + gq);
     const int32_t* row = idx + (valid ? n : 0) * GK;
     auto group_mask = [&](int g) -> uint64_t {
         uint64_t pm = 0;
@@ -197,22 +229,22 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
         }
         return pm;
     };
-    for (int g = 0; g < G; ++g) {
+    for (int g = g0; g < g1; ++g) {
         const uint64_t pm = group_mask(g);
         for (int m = 0; m < M; ++m) {
             const uint64_t mask = __builtin_amdgcn_ballot_w64((pm >> m) & 1ull);
-            if ((tid & 63) == 0) wtot[wave][g * M + m] = __builtin_popcountll(mask);
+            if ((tid & 63) == 0) wtot[wq][g * M + m] = __builtin_popcountll(mask);
         }
     }
     __syncthreads();
-    for (int g = 0; g < G; ++g) {
+    for (int g = g0; g < g1; ++g) {
         const uint64_t pm = group_mask(g);
         for (int m = 0; m < M; ++m) {
             const uint64_t mask = __builtin_amdgcn_ballot_w64((pm >> m) & 1ull);
             if (!((pm >> m) & 1ull)) continue;
             const int e = g * M + m;
             int pos = base[e];
-            for (int w = 0; w < wave; ++w) pos += wtot[w][e];
+            for (int w = 0; w < wq; ++w) pos += wtot[w][e];
             pos += __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
             int r = 0;
             while (row[g * k + r] != m) ++r;            // the first rank that picked m (bit set: one exists)
