@@ -549,7 +549,6 @@ __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(Cfg::W
     __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     __shared__ __attribute__((aligned(16))) char lds_b[Cfg::STAGE_BYTES];
     char* lds1 = lds_b;
-    __shared__ int32_t s_dst[Cfg::BM];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int64_t j = blockIdx.x / 8;
@@ -571,13 +570,20 @@ __global__ __launch_bounds__(Cfg::NTH) __attribute__((amdgpu_waves_per_eu(Cfg::W
         const int r = rb + tid / 8 + Cfg::RPP * i;
         a_row[i] = (const T*)a.X + (int64_t)a.perm[r < re ? r : rb] * a.ldx + (tid & 7) * Cfg::VEC;
     }
-    for (int r = tid; r < Cfg::BM; r += Cfg::NTH) s_dst[r] = (rb + r < re) ? a.dst[rb + r] : -1;
-    // Swapped operands: a lane holds output columns c .. c+3 of tile row r.
-    f32x4 acc[Cfg::FM][Cfg::FN];
-    gemm_kloop<T, Cfg, true>(lds, lds1, a_row, b_row, a.K, acc);   // its barriers publish s_dst
+    // Destination rows of the tile rows this lane stores, read before the K
+    // loop so their latency hides behind it.
+    int drows[Cfg::FM];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-        const int drow = s_dst[(wm * Cfg::FM + i) * 16 + (lane & 15)];
+        const int r = rb + (wm * Cfg::FM + i) * 16 + (lane & 15);
+        drows[i] = r < re ? a.dst[r] : -1;
+    }
+    // Swapped operands: a lane holds output columns c .. c+3 of tile row r.
+    f32x4 acc[Cfg::FM][Cfg::FN];
+    gemm_kloop<T, Cfg, true>(lds, lds1, a_row, b_row, a.K, acc);
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const int drow = drows[i];
         if (drow < 0) continue;
 #pragma unroll
         for (int jb = 0; jb < Cfg::FN; ++jb) {

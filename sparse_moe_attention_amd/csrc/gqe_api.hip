@@ -37,14 +37,16 @@ namespace {
 #endif
 using ProjBf16 = TileCfg<bf16, GQE_PROJ_CFG>;
 using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
-// The grouped routed-Q GEMM: 128 x 64 tiles (one expert's 64 query columns),
-// three workgroups per CU (its registers fit three waves per SIMD and its two
-// LDS stages take 48 KB): its K steps are short (8 MFMAs per wave), so the
-// extra workgroup hides the tile loads (T = 32K: 72 -> 59 us). The projection
-// GEMM keeps two 128 x 128 workgroups per CU; 128 x 64 or 64 x 128 tiles at
-// three per CU measured slower there (106 -> 121 us).
+// The grouped routed-Q GEMM: 256 x 64 tiles (256 rows of one expert's
+// segment, its 64 query columns), eight waves of 32 x 64, two workgroups per
+// CU (80 KB of LDS each, 86 VGPRs), so four waves per SIMD. A wave's K step
+// is short (8 MFMAs per 32-wide step), so the tile loads need many waves to
+// hide behind: against 128 x 64 tiles at two per CU, 72 -> 58 us at T = 32K
+// and 367 -> 288 us on the k = 2, D = 2048 workload. The projection GEMM keeps
+// two 128 x 128 workgroups per CU; 128 x 64 or 64 x 128 tiles at three per CU
+// measured slower there (106 -> 121 us).
 #ifndef GQE_GRP_CFG
-#define GQE_GRP_CFG 128, 64, 4, 1, 3
+#define GQE_GRP_CFG 256, 64, 8, 1, 4
 #endif
 using GrpBf16 = TileCfg<bf16, GQE_GRP_CFG>;
 using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
