@@ -32,8 +32,11 @@ using namespace gqe;
 
 namespace {
 
+// Projection GEMM: 128 x 128 tiles of eight waves (32 x 64 each), two
+// workgroups per CU, four waves per SIMD (T = 32K: K/V projection 107 -> 103
+// us, Wo 83 -> 79 us against four waves of 64 x 64).
 #ifndef GQE_PROJ_CFG
-#define GQE_PROJ_CFG 128, 128, 2, 2, 2
+#define GQE_PROJ_CFG 128, 128, 4, 2, 4
 #endif
 using ProjBf16 = TileCfg<bf16, GQE_PROJ_CFG>;
 using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
@@ -42,9 +45,7 @@ using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
 // CU (80 KB of LDS each, 86 VGPRs), so four waves per SIMD. A wave's K step
 // is short (8 MFMAs per 32-wide step), so the tile loads need many waves to
 // hide behind: against 128 x 64 tiles at two per CU, 72 -> 58 us at T = 32K
-// and 367 -> 288 us on the k = 2, D = 2048 workload. The projection GEMM keeps
-// two 128 x 128 workgroups per CU; 128 x 64 or 64 x 128 tiles at three per CU
-// measured slower there (106 -> 121 us).
+// and 367 -> 288 us on the k = 2, D = 2048 workload.
 #ifndef GQE_GRP_CFG
 #define GQE_GRP_CFG 256, 64, 8, 1, 4
 #endif
