@@ -263,8 +263,9 @@ gqe_status gqe_attn_bwd_timed(const gqe_shape* s, const void* x, const void* Wr,
  * projections, and so the KV cache, of the underlying GQA model unchanged;
  * only the query side is sparse ([GQE-x] "Architecture and routing"; [GQE-n]
  * part 4). Full layer (GQE_FULL), bf16.
- *   s          B sequences; T = cache capacity per sequence (a multiple of 32);
- *              D, G, M, k, d_h, shared_kv_group as for the layer
+ *   s          B sequences; T = cache capacity per sequence (a multiple of 32,
+ *              with one group's values, d_h*B*T*2 bytes, under 4 GiB; else
+ *              GQE_ERR_SHAPE); D, G, M, k, d_h, shared_kv_group as for the layer
  *   pos        [B] int32, device: sequence b has pos[b] cached positions and the
  *              new token goes at position pos[b] (0 <= pos[b] < T; an entry
  *              outside that range leaves its cache untouched and its outputs

@@ -125,6 +125,50 @@ struct DecodeArgs {
 #ifndef GQE_DEC_WPE
 #define GQE_DEC_WPE 2
 #endif
+#ifndef GQE_DEC_LINES
+#define GQE_DEC_LINES 1
+#endif
+
+// Key (within a 64-key step) of row i of score block kb when K is read in
+// whole lines: block pairs (2h, 2h + 1) give product step h its keys
+// 16*q4 + 8*h + e, matching the V^T fragments lines_to_frags builds.
+__device__ __forceinline__ int dec_key(int kb, int i) {
+    return 16 * (i >> 2) + 8 * (kb >> 1) + 4 * (kb & 1) + (i & 3);
+}
+
+// Two whole-line loads of 16 rows (a: rows 0-7, b: rows 8-15; lane (l16, q4)
+// holds row l16 & 7 of its half, 16-byte chunk (l16 >> 3) + 2*q4) become two
+// MFMA fragments: lane (l16, q4) of a / b then holds row l16, chunk 2*q4 / 2*q4 + 1.
+// Lanes l16 and l16 ^ 8 trade one register's worth: a row rotation by 8 lanes
+// written to half of each row's lanes.
+__device__ __forceinline__ void lines_to_frags(u32x4& a, u32x4& b) {
+    u32x4 f0, f1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f0[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)a[i], (int)b[i], 0x128, 0xF, 0xC, false);
+        f1[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)b[i], (int)a[i], 0x128, 0xF, 0x3, false);
+    }
+    a = f0;
+    b = f1;
+}
+
+__device__ __forceinline__ Frag<bf16> as_frag(u32x4 u) {
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, u);
+    return f;
+}
+
+// A raw buffer view of n bytes at p (p uniform over the wave).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+// A 16-byte streaming buffer load at byte offset off (per lane): the cache is
+// read once, so its lines need not stay in L2. Offsets at or past the view's
+// size read as zeros (the whole offset is the lane's, so the check sees it).
+__device__ __forceinline__ u32x4 ld16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
 constexpr int kDecNW = 4;          // waves per workgroup
 constexpr int kDecCW = GQE_DEC_CW; // keys per wave
 constexpr int kDecCH = kDecNW * kDecCW;
@@ -136,6 +180,9 @@ void attn_decode_kernel(DecodeArgs a) {
     constexpr int KS = 64;                          // keys per step
     constexpr int KB = KS / 16, KH = KS / 32;       // 16-key score blocks, 32-key product steps
     constexpr int NB = kDecCW / KS;                 // steps per wave
+    constexpr bool kLines = GQE_DEC_LINES && D % 64 == 0;
+    // Key of row i of score block kb (rows 4*q4 + v of a lane's result).
+    auto row_key = [](int kb, int i) { return kLines ? dec_key(kb, i) : key_of_row(kb, i); };
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -150,6 +197,12 @@ void attn_decode_kernel(DecodeArgs a) {
     const bf16* Kg = a.K + ((int64_t)g * a.Bt + b) * a.T * D;
     const int64_t vrow = (int64_t)a.Bt * a.T;
     const bf16* Vg = a.Vt + (int64_t)g * D * vrow + (int64_t)b * a.T;
+    // Buffer views (sizes below 4 GiB by the host's checks): this sequence's
+    // K rows, and V^T from its first column to the end of its last row.
+    const __amdgpu_buffer_rsrc_t rsK = make_rsrc(Kg, (uint32_t)(a.T * 2 * D));
+    const __amdgpu_buffer_rsrc_t rsV = make_rsrc(Vg, (uint32_t)(((int64_t)(D - 1) * vrow + a.T) * 2));
+    const uint32_t kvoff = (uint32_t)((16 * ((l16 >> 2) & 1) + (l16 & 3)) * (2 * D) + 16 * ((l16 >> 3) + 2 * q4));
+    const uint32_t vvoff = (uint32_t)((l16 & 7) * vrow * 2 + 16 * ((l16 >> 3) + 2 * q4));
 
     __shared__ float s_m[kDecNW][16], s_l[kDecNW][16];
     __shared__ float s_o[kDecNW][D][16];
@@ -162,7 +215,7 @@ void attn_decode_kernel(DecodeArgs a) {
                                   : (hd < Rg ? a.Qsh + (int64_t)b * D : nullptr);
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) {
-            if (qp != nullptr) qf[dk] = ld_frag<bf16>(qp + dk * 32 + 8 * q4);
+            if (qp != nullptr) qf[dk] = ld_frag<bf16>(qp + (kLines ? 64 * (dk >> 1) + 16 * q4 + 8 * (dk & 1) : dk * 32 + 8 * q4));
             else qf[dk].v = bf16x8{};
         }
         Frag<bf16> ones;
@@ -175,38 +228,70 @@ void attn_decode_kernel(DecodeArgs a) {
 
         const int64_t w0 = c0 + (int64_t)wave * kDecCW;
         const int nb = (int)max<int64_t>(0, min<int64_t>(NB, (len - w0 + KS - 1) / KS));
-        // Operand fragments of one step of KS keys: K rows (A of S^T) and
-        // V^T rows (A of O^T). Each V^T row's KS keys (128 bytes) are
-        // requested together. Keys past the cache end (the last step of a
-        // sequence whose T is not a multiple of KS) read the last row
-        // instead; they lie past len, so they are masked below.
-        auto load = [&](int j, Frag<bf16> (&kf)[KB][DK], Frag<bf16> (&vf)[KH][CB]) {
+        // The loads of one step of KS keys: K rows (A of S^T) and V^T rows
+        // (A of O^T), KS keys (128 bytes) of each V^T row. With kLines each
+        // load instruction reads whole 128-byte lines (8 rows, lane (l16, q4)
+        // taking row l16 & 7 of its half and 16-byte chunk (l16 >> 3) + 2*q4)
+        // as streaming buffer loads, and lines_to_frags then trades halves
+        // between lanes l16 and l16 ^ 8, which leaves chunk 2*q4 + h of row
+        // l16 in register h: fragment h's contraction element 8*q4 + e is d
+        // (or key) 16*q4 + 8*h + e, on K, Q and V^T alike. Rows past the cache
+        // end (the last step when T is not a multiple of KS) lie outside the
+        // K buffer and read as zeros; their V^T columns read the next row's
+        // first keys (or zeros after the last row). Otherwise (d = 32, whose
+        // fragments already cover whole lines of K) each lane loads its
+        // fragment directly and keys past the cache end read the last row.
+        // Either way those keys lie past len and are masked below.
+        auto load = [&](int j, u32x4 (&kl)[KB][DK], u32x4 (&vl)[CB][KH]) {
             const int64_t k0 = w0 + (int64_t)KS * j;
-            const bool tail = k0 + KS > a.T;
+            if constexpr (kLines) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                int64_t kr = k0 + key_of_row(kb, l16);
-                if (tail) kr = min<int64_t>(kr, a.T - 1);
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int dk = 0; dk < DK; ++dk) kf[kb][dk] = ld_frag<bf16>(Kg + kr * D + dk * 32 + 8 * q4);
-            }
+                    for (int dk = 0; dk < DK; ++dk) {
+                        const int64_t key = k0 + 32 * (dk & 1) + 8 * (kb >> 1) + 4 * (kb & 1);   // + the lane's rows
+                        kl[kb][dk] = ld16_buf(rsK, kvoff + (uint32_t)(key * (2 * D) + 128 * (dk >> 1)));
+                    }
 #pragma unroll
-            for (int h = 0; h < KH; ++h) {
-                int64_t kc = k0 + 32 * h + 8 * q4;
-                if (tail) kc = min<int64_t>(kc, a.T - 8);
+                for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) vf[h][cb] = ld_frag<bf16>(Vg + (int64_t)(cb * 16 + l16) * vrow + kc);
+                    for (int h = 0; h < KH; ++h)
+                        vl[cb][h] = ld16_buf(rsV, vvoff + (uint32_t)(((int64_t)(16 * cb + 8 * h) * vrow + k0) * 2));
+            } else {
+                const bool tail = k0 + KS > a.T;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    int64_t kr = k0 + key_of_row(kb, l16);
+                    if (tail) kr = min<int64_t>(kr, a.T - 1);
+#pragma unroll
+                    for (int dk = 0; dk < DK; ++dk) kl[kb][dk] = ld16(Kg + kr * D + dk * 32 + 8 * q4);
+                }
+#pragma unroll
+                for (int h = 0; h < KH; ++h) {
+                    int64_t kc = k0 + 32 * h + 8 * q4;
+                    if (tail) kc = min<int64_t>(kc, a.T - 8);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) vl[cb][h] = ld16(Vg + (int64_t)(cb * 16 + l16) * vrow + kc);
+                }
             }
         };
-        Frag<bf16> kA[KB][DK], vA[KH][CB], kB[KB][DK], vB[KH][CB];
-        auto compute = [&](int j, const Frag<bf16> (&kf)[KB][DK], Frag<bf16> (&vf)[KH][CB]) {
+        u32x4 kA[KB][DK], vA[CB][KH], kB[KB][DK], vB[CB][KH];
+        auto compute = [&](int j, u32x4 (&kl)[KB][DK], u32x4 (&vl)[CB][KH]) {
             const int64_t k0 = w0 + (int64_t)KS * j;
+            if constexpr (kLines) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int dk = 0; dk < DK; dk += 2) lines_to_frags(kl[kb][dk], kl[kb][dk + 1]);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) lines_to_frags(vl[cb][0], vl[cb][1]);
+            }
             f32x4 s[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int dk = 0; dk < DK; ++dk) s[kb] = mma16(kf[kb][dk], qf[dk], s[kb]);
+                for (int dk = 0; dk < DK; ++dk) s[kb] = mma16(as_frag(kl[kb][dk]), qf[dk], s[kb]);
             }
             if (k0 + KS > len) {
                 // Keys at or past len are not attended: their scores become -inf
@@ -216,14 +301,18 @@ void attn_decode_kernel(DecodeArgs a) {
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        if (k0 + key_of_row(kb, 4 * q4 + v) >= len) s[kb][v] = -INFINITY;
+                        if (k0 + row_key(kb, 4 * q4 + v) >= len) s[kb][v] = -INFINITY;
 #pragma unroll
                 for (int h = 0; h < KH; ++h)
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            if (k0 + 32 * h + 8 * q4 + i >= len) vf[h][cb].v[i] = (bf16)0.f;
+                        for (int i = 0; i < 4; ++i) {
+                            // dword i holds keys 2i (low half) and 2i + 1 (high half)
+                            const int64_t key = k0 + (kLines ? 16 * q4 + 8 * h : 32 * h + 8 * q4) + 2 * i;
+                            if (key >= len) vl[cb][h][i] = 0u;
+                            else if (key + 1 >= len) vl[cb][h][i] &= 0xffffu;
+                        }
             }
             float mx = s[0][0];
 #pragma unroll
@@ -247,7 +336,7 @@ void attn_decode_kernel(DecodeArgs a) {
                 }
                 lsum = mma16(ones, pf, lsum);
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) o[cb] = mma16(vf[h][cb], pf, o[cb]);
+                for (int cb = 0; cb < CB; ++cb) o[cb] = mma16(as_frag(vl[cb][h]), pf, o[cb]);
             }
         };
         // Two register sets: the next step's loads are in flight during this step's products.

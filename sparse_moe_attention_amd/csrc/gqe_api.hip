@@ -703,7 +703,9 @@ gqe_status check_decode(const gqe_shape* s, Dims* cache, Dims* tok) {
     gqe_status rc = check_shape(s, cache);
     if (rc != GQE_OK) return rc;
     if (cache->f32 || cache->variant != GQE_FULL) return GQE_ERR_UNSUPPORTED;
-    if (s->T % 32 != 0) return GQE_ERR_SHAPE;                // cache rows read in 32-key steps
+    if (s->T % 32 != 0) return GQE_ERR_SHAPE;                // 8-key V^T pieces never straddle T
+    // The attention reads one group's V^T (d x B*T) through a 32-bit buffer view.
+    if ((int64_t)s->d_h * s->B * s->T * 2 > (int64_t)UINT32_MAX) return GQE_ERR_SHAPE;
     gqe_shape t = *s;
     t.T = 1;
     return check_shape(&t, tok);

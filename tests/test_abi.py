@@ -182,3 +182,15 @@ def test_decode_entry_point_validates(lib):
     assert lib.gqe_decode_workspace_bytes(ctypes.byref(shape(T=250))) == 0
     for kw in (dict(dtype=gq.GQE_F32), dict(variant=gq.GQE_NO_SHARED)):
         assert call(shape(T=256, **kw), 1 << 40) == -3
+
+
+def test_decode_shape_errors(lib):
+    """The decode step needs T a multiple of 32 and one group's values
+    (d_h * B * T * 2 bytes) under 4 GiB; both are refused before any HIP call."""
+    ok = shape(B=16, T=1 << 20, D=1024, G=8, M=2, d_h=64)          # 2 GiB of values per group
+    assert lib.gqe_decode_workspace_bytes(ctypes.byref(ok)) > 0
+    for bad in (shape(T=112), shape(B=32, T=1 << 20, D=1024, G=8, M=2, d_h=64)):
+        assert lib.gqe_decode_workspace_bytes(ctypes.byref(bad)) == 0
+        rc = lib.gqe_decode_step(ctypes.byref(bad), A, A, A, None, A, A, A, A, A, A, A, A, None, None, A,
+                                 1 << 40, None)
+        assert rc == -2

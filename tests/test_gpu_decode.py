@@ -34,6 +34,11 @@ CASES = {
     "max_pool_256_experts": (Shape(B=2, T=192, D=64, G=4, M=64, k=3, d=32, router_bias=True, shared_kv_group=3),
                              [100, 191]),
     "many_sequences": (Shape(B=33, T=64, D=64, G=2, M=2, k=1, d=64), [(7 * b) % 64 for b in range(33)]),
+    # T = 32 mod 64 at d = 64: a sequence's last 64-key step reaches past the cache end (those K rows
+    # read as zeros, those V^T columns as the next row's first keys or zeros), in the last sequence too
+    "tail_past_cache_end": (Shape(B=3, T=96, D=128, G=2, M=3, k=2, d=64, router_bias=True, shared_kv_group=1),
+                            [95, 70, 64]),
+    "two_chunks_tail": (Shape(B=2, T=2080, D=64, G=2, M=2, k=1, d=64), [2050, 2079]),
     # more than 64 new tokens: the token projections take the tiled GEMM instead of the skinny one
     "seventy_sequences": (Shape(B=70, T=32, D=64, G=2, M=2, k=1, d=32, shared_kv_group=1),
                           [(5 * b) % 32 for b in range(70)]),
