@@ -406,11 +406,14 @@ void attn_fwd_kernel(AttnArgs a) {
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) mx = vmax(mx, s[kb][qb][v]);
-                mx = quad_row_max(mx);
                 // Move the reference only when needed: first tile, or scores
-                // more than kLazyRescale above it.
-                const bool need = mx > thr[qb];
-                if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                // more than kLazyRescale above it. A column passes the
+                // threshold exactly when one of its four lanes' shares does, so
+                // the shares decide first and the column maximum is formed only
+                // when some column moves.
+                if (__builtin_amdgcn_ballot_w64(mx > thr[qb]) != 0) {
+                    mx = quad_row_max(mx);
+                    const bool need = mx > thr[qb];
                     const float delta = need ? mx : 0.f;
                     const float corr = __builtin_amdgcn_exp2f(-delta);
                     minit[qb] -= delta;
