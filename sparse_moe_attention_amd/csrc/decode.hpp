@@ -119,9 +119,6 @@ struct DecodeArgs {
     int32_t R16;          // head slots per group, a multiple of 16 (>= k + 1)
 };
 
-#ifndef GQE_DEC_CW
-#define GQE_DEC_CW 512
-#endif
 #ifndef GQE_DEC_WPE
 #define GQE_DEC_WPE 2
 #endif
@@ -170,16 +167,15 @@ __device__ __forceinline__ u32x4 ld16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
 }
 constexpr int kDecNW = 4;          // waves per workgroup
-constexpr int kDecCW = GQE_DEC_CW; // keys per wave
-constexpr int kDecCH = kDecNW * kDecCW;
 
-template <int D>
+// CW keys per wave, kDecNW * CW per chunk (workgroup).
+template <int D, int CW>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(GQE_DEC_WPE)))
 void attn_decode_kernel(DecodeArgs a) {
     constexpr int DK = D / 32, CB = D / 16;
     constexpr int KS = 64;                          // keys per step
     constexpr int KB = KS / 16, KH = KS / 32;       // 16-key score blocks, 32-key product steps
-    constexpr int NB = kDecCW / KS;                 // steps per wave
+    constexpr int NB = CW / KS;                     // steps per wave
     constexpr bool kLines = GQE_DEC_LINES && D % 64 == 0;
     // Key of row i of score block kb (rows 4*q4 + v of a lane's result).
     auto row_key = [](int kb, int i) { return kLines ? dec_key(kb, i) : key_of_row(kb, i); };
@@ -191,7 +187,7 @@ void attn_decode_kernel(DecodeArgs a) {
     const int64_t p = a.pos[b];
     if (p < 0 || p >= a.T) return;                  // not a cache position: nothing is read
     const int64_t len = p + 1;                      // keys 0 .. pos[b]
-    const int64_t c0 = (int64_t)ch * kDecCH;
+    const int64_t c0 = (int64_t)ch * (kDecNW * CW);
     if (c0 >= len) return;                          // the combine reads chunks below len only
     const int Rg = a.k + (g == a.s0 ? 1 : 0);
     const bf16* Kg = a.K + ((int64_t)g * a.Bt + b) * a.T * D;
@@ -226,7 +222,7 @@ void attn_decode_kernel(DecodeArgs a) {
         for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = -INFINITY;                         // running max of head l16 (log2 units)
 
-        const int64_t w0 = c0 + (int64_t)wave * kDecCW;
+        const int64_t w0 = c0 + (int64_t)wave * CW;
         const int nb = (int)max<int64_t>(0, min<int64_t>(NB, (len - w0 + KS - 1) / KS));
         // The loads of one step of KS keys: K rows (A of S^T) and V^T rows
         // (A of O^T), KS keys (128 bytes) of each V^T row. With kLines each
@@ -392,13 +388,13 @@ void attn_decode_kernel(DecodeArgs a) {
 // column c of the chunks' outputs with eight chunks' loads in flight.
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* part_o, const float* part_ml,
                                                             const int32_t* pos, bf16* C, int G, int k, int s0, int d,
-                                                            int n_ch, int R16, int64_t ldc, int64_t T) {
+                                                            int n_ch, int ch_keys, int R16, int64_t ldc, int64_t T) {
     const int GK = G * k;
     const int b = blockIdx.x / (GK + 1), j = blockIdx.x % (GK + 1), lane = threadIdx.x;
     const int64_t p = pos[b];
     // An out-of-range position reads no chunk (its slots are unspecified).
     const int64_t len = (p < 0 || p >= T) ? 0 : p + 1;
-    const int nch = (int)min<int64_t>(n_ch, (len + kDecCH - 1) / kDecCH);
+    const int nch = (int)min<int64_t>(n_ch, (len + ch_keys - 1) / ch_keys);
     if (nch == 0) return;
     const int g = j < GK ? j / k : s0, hd = j < GK ? j % k : k;   // the shared head is group s0's row k
     const int64_t hb = (((int64_t)b * G + g) * n_ch) * R16 + hd;

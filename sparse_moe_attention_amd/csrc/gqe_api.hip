@@ -714,13 +714,17 @@ gqe_status check_decode(const gqe_shape* s, Dims* cache, Dims* tok) {
 struct DecodeWs {
     GqeWs tok;
     size_t Kn, Vn, part_o, part_ml, total;
-    int n_ch, R16;
+    int cw, n_ch, R16;    // keys per wave of the cache attention, chunks per sequence, head slots
 };
 
 DecodeWs decode_layout(const Dims& c, const Dims& t) {
     DecodeWs L;
     L.tok = gqe_layout(t);
-    L.n_ch = (int)((c.T + kDecCH - 1) / kDecCH);
+    // The largest of 512, 256 and 128 keys per wave that still launches 512
+    // workgroups (two per CU): a short cache takes shorter chunks.
+    L.cw = 512;
+    while (L.cw > 128 && (int64_t)c.B * c.G * ((c.T + kDecNW * L.cw - 1) / (kDecNW * L.cw)) < 512) L.cw /= 2;
+    L.n_ch = (int)((c.T + kDecNW * L.cw - 1) / (kDecNW * L.cw));
     L.R16 = (int)align_up((size_t)(c.k + 1), 16);
     size_t o = L.tok.total;
     auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
@@ -813,13 +817,22 @@ gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, co
     a.n_ch = L.n_ch;
     a.R16 = L.R16;
     const dim3 grid((unsigned)((int64_t)c.B * c.G * L.n_ch));
-    if (c.d == 64) hipLaunchKernelGGL(attn_decode_kernel<64>, grid, dim3(kDecNW * 64), 0, st, a);
-    else hipLaunchKernelGGL(attn_decode_kernel<32>, grid, dim3(kDecNW * 64), 0, st, a);
+    const dim3 blk(kDecNW * 64);
+    if (c.d == 64) {
+        if (L.cw == 512) hipLaunchKernelGGL((attn_decode_kernel<64, 512>), grid, blk, 0, st, a);
+        else if (L.cw == 256) hipLaunchKernelGGL((attn_decode_kernel<64, 256>), grid, blk, 0, st, a);
+        else hipLaunchKernelGGL((attn_decode_kernel<64, 128>), grid, blk, 0, st, a);
+    } else {
+        if (L.cw == 512) hipLaunchKernelGGL((attn_decode_kernel<32, 512>), grid, blk, 0, st, a);
+        else if (L.cw == 256) hipLaunchKernelGGL((attn_decode_kernel<32, 256>), grid, blk, 0, st, a);
+        else hipLaunchKernelGGL((attn_decode_kernel<32, 128>), grid, blk, 0, st, a);
+    }
     mk.at(2);
     bf16* C = (bf16*)at(ws, F.C);
     const int64_t ldc = (int64_t)c.slots * c.d;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(c.B * (c.GK + 1))), dim3(64), 0, st,
-                       (const float*)a.part_o, (const float*)a.part_ml, pos, C, c.G, c.k, c.s0, c.d, L.n_ch, L.R16, ldc,
+                       (const float*)a.part_o, (const float*)a.part_ml, pos, C, c.G, c.k, c.s0, c.d, L.n_ch,
+                       kDecNW * L.cw, L.R16, ldc,
                        c.T);
     run_combine(t, C, w, st);
     SegList so = proj_base(t, C, ldc, t.N, (int)ldc);
