@@ -19,8 +19,9 @@
 //     accumulates their dK^T, dV^T over every query row at or after the
 //     keys, 64 rows per step staged in LDS (Q, dO row-major for the score
 //     products, Q^T and dO^T for the accumulations, lse and delta);
-//   * attn_bwd_dq_kernel: one workgroup per (group, sequence, 256 rows) as
-//     in the forward; each wave keeps its 32 rows' Q and dO resident and
+//   * attn_bwd_dq_kernel: one workgroup per (group, sequence, 128 rows: four
+//     waves of 32), three per CU as in the forward; each wave keeps its 32
+//     rows' Q and dO resident and
 //     walks the key tiles up to its last token, staging K, V (row-major) and
 //     K^T in LDS, accumulating dQ^T = K^T dS^T.
 // Score blocks are oriented so that the probabilities / score gradients a
