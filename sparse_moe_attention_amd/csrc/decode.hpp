@@ -15,9 +15,9 @@
 //     O^T = V^T P^T) for all query heads of the group at once (the picked
 //     experts and, on its group, the shared head, zero-padded to 16), with an
 //     online softmax, and writes the chunk's (max, sum, unnormalised output);
-//   * decode_combine_kernel: merges the chunks of every head into its slot of
-//     C = [hard | weighted | shared] (the weighted slot is then formed by the
-//     prefill's combine kernel) for the output projection, again a
+//   * decode_combine_kernel: per sequence, merges the chunks of every head
+//     into its slot of C = [hard | weighted | shared] and then forms the
+//     weighted slot from the hard ones, for the output projection, again a
 //     skinny_proj_kernel pass.
 // The cache layout is the prefill's: keys [G][B][T][d] (one contiguous row
 // per key), values transposed [G][d][B*T] (contiguous keys per column).
@@ -380,49 +380,64 @@ void attn_decode_kernel(DecodeArgs a) {
     }
 }
 
-// Merges the chunks of one head of one sequence (workgroup (b, j): routed
-// head j = g*k + r, or j = G*k for the shared head) and writes its slot of
-// C[b] = [O_0 .. O_{Gk-1} | weighted | O_sh] in bf16. The weighted slot is
-// formed afterwards from the bf16 hard slots, as in the prefill. One wave:
-// the lanes read the chunks' (max, sum) pairs 64 at a time, then lane c sums
-// column c of the chunks' outputs with eight chunks' loads in flight.
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float* part_o, const float* part_ml,
-                                                            const int32_t* pos, bf16* C, int G, int k, int s0, int d,
-                                                            int n_ch, int ch_keys, int R16, int64_t ldc, int64_t T) {
+// Merges the chunks of every head of one sequence (workgroup b; head j =
+// g*k + r for routed head r of group g, j = G*k for the shared head) into
+// its slot of C[b] = [O_0 .. O_{Gk-1} | weighted | O_sh] in bf16, then forms
+// the weighted slot from the bf16 hard slots as the prefill's combine does
+// (fp32 sum in slot order). One wave per head at a time (heads wave, wave +
+// waves, ...): the lanes read the chunks' (max, sum) pairs 64 at a time,
+// then lane c sums column c of the chunks' outputs with eight chunks' loads
+// in flight.
+constexpr int kDecCombMaxWaves = 16;
+__global__ __launch_bounds__(kDecCombMaxWaves * 64) void decode_combine_kernel(
+    const float* part_o, const float* part_ml, const float* w, const int32_t* pos, bf16* C, int G, int k, int s0,
+    int d, int n_ch, int ch_keys, int R16, int64_t ldc, int64_t T) {
     const int GK = G * k;
-    const int b = blockIdx.x / (GK + 1), j = blockIdx.x % (GK + 1), lane = threadIdx.x;
+    const int b = blockIdx.x, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
     const int64_t p = pos[b];
     // An out-of-range position reads no chunk (its slots are unspecified).
     const int64_t len = (p < 0 || p >= T) ? 0 : p + 1;
     const int nch = (int)min<int64_t>(n_ch, (len + ch_keys - 1) / ch_keys);
-    if (nch == 0) return;
-    const int g = j < GK ? j / k : s0, hd = j < GK ? j % k : k;   // the shared head is group s0's row k
-    const int64_t hb = (((int64_t)b * G + g) * n_ch) * R16 + hd;
-    const float* ml = part_ml + hb * 2;
-    const int64_t mls = (int64_t)R16 * 2;
-    float M = -INFINITY;
-    for (int i = lane; i < nch; i += 64) M = vmax(M, ml[i * mls]);
-    for (int o = 32; o > 0; o >>= 1) M = vmax(M, __shfl_xor(M, o));
-    float sl = 0.f;
-    for (int i = lane; i < nch; i += 64) sl += __builtin_amdgcn_exp2f(ml[i * mls] - M) * ml[i * mls + 1];
-    for (int o = 32; o > 0; o >>= 1) sl += __shfl_xor(sl, o);
-    if (lane >= d) return;
-    const float* po = part_o + hb * d + lane;
-    const int64_t pos_ = (int64_t)R16 * d;
-    float so = 0.f;
-    int i = 0;
-    for (; i + 8 <= nch; i += 8) {
-        float f[8], v[8];
+    if (nch == 0) return;                                         // uniform over the workgroup
+    bf16* Cb = C + (int64_t)b * ldc;
+    for (int j = wave; j <= GK; j += nw) {
+        const int g = j < GK ? j / k : s0, hd = j < GK ? j % k : k;   // the shared head is group s0's row k
+        const int64_t hb = (((int64_t)b * G + g) * n_ch) * R16 + hd;
+        const float* ml = part_ml + hb * 2;
+        const int64_t mls = (int64_t)R16 * 2;
+        float M = -INFINITY;
+        for (int i = lane; i < nch; i += 64) M = vmax(M, ml[i * mls]);
+        for (int o = 32; o > 0; o >>= 1) M = vmax(M, __shfl_xor(M, o));
+        float sl = 0.f;
+        for (int i = lane; i < nch; i += 64) sl += __builtin_amdgcn_exp2f(ml[i * mls] - M) * ml[i * mls + 1];
+        for (int o = 32; o > 0; o >>= 1) sl += __shfl_xor(sl, o);
+        if (lane < d) {
+            const float* po = part_o + hb * d + lane;
+            const int64_t pos_ = (int64_t)R16 * d;
+            float so = 0.f;
+            int i = 0;
+            for (; i + 8 <= nch; i += 8) {
+                float f[8], v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            f[q] = ml[(i + q) * mls];
-            v[q] = po[(i + q) * pos_];
+                for (int q = 0; q < 8; ++q) {
+                    f[q] = ml[(i + q) * mls];
+                    v[q] = po[(i + q) * pos_];
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) so += __builtin_amdgcn_exp2f(f[q] - M) * v[q];
+            }
+            for (; i < nch; ++i) so += __builtin_amdgcn_exp2f(ml[i * mls] - M) * po[i * pos_];
+            Cb[(j < GK ? (int64_t)j : (int64_t)GK + 1) * d + lane] = (bf16)(so / sl);
         }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) so += __builtin_amdgcn_exp2f(f[q] - M) * v[q];
     }
-    for (; i < nch; ++i) so += __builtin_amdgcn_exp2f(ml[i * mls] - M) * po[i * pos_];
-    C[(int64_t)b * ldc + (j < GK ? (int64_t)j : (int64_t)GK + 1) * d + lane] = (bf16)(so / sl);
+    __syncthreads();   // the hard slots written above, visible to the whole workgroup
+    const float* wb = w + (int64_t)b * GK;
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+        float acc = 0.f;
+        for (int si = 0; si < GK; ++si) acc += wb[si] * (float)Cb[(int64_t)si * d + c];
+        Cb[(int64_t)GK * d + c] = (bf16)acc;
+    }
 }
 
 }  // namespace gqe

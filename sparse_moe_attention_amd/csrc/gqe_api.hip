@@ -830,11 +830,10 @@ gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, co
     mk.at(2);
     bf16* C = (bf16*)at(ws, F.C);
     const int64_t ldc = (int64_t)c.slots * c.d;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(c.B * (c.GK + 1))), dim3(64), 0, st,
-                       (const float*)a.part_o, (const float*)a.part_ml, pos, C, c.G, c.k, c.s0, c.d, L.n_ch,
-                       kDecNW * L.cw, L.R16, ldc,
-                       c.T);
-    run_combine(t, C, w, st);
+    const int comb_waves = std::min(c.GK + 1, kDecCombMaxWaves);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)c.B), dim3(comb_waves * 64), 0, st,
+                       (const float*)a.part_o, (const float*)a.part_ml, (const float*)w, pos, C, c.G, c.k, c.s0, c.d,
+                       L.n_ch, kDecNW * L.cw, L.R16, ldc, c.T);
     SegList so = proj_base(t, C, ldc, t.N, (int)ldc);
     so.add(Wo, (int)c.D, out, OUT_ROWS, c.D, nullptr);
     run_proj_rows(t, so, st);
