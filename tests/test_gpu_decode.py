@@ -39,6 +39,11 @@ CASES = {
     "tail_past_cache_end": (Shape(B=3, T=96, D=128, G=2, M=3, k=2, d=64, router_bias=True, shared_kv_group=1),
                             [95, 70, 64]),
     "two_chunks_tail": (Shape(B=2, T=2080, D=64, G=2, M=2, k=1, d=64), [2050, 2079]),
+    # chunk lengths: the launch takes 512, 256 or 128 keys per wave, the largest that still gives
+    # 512 workgroups (B * G * chunks); these two take 256 and 512 with ragged positions
+    "chunks_of_1024_keys": (Shape(B=4, T=16384, D=128, G=8, M=2, k=1, d=64), [16383, 9000, 1025, 4096]),
+    "chunks_of_2048_keys": (Shape(B=8, T=16384, D=64, G=8, M=2, k=1, d=64, router_bias=True),
+                            [16383, 0, 2047, 2048, 12345, 8191, 100, 16000]),
     # more than 64 new tokens: the token projections take the tiled GEMM instead of the skinny one
     "seventy_sequences": (Shape(B=70, T=32, D=64, G=2, M=2, k=1, d=32, shared_kv_group=1),
                           [(5 * b) % 32 for b in range(70)]),
