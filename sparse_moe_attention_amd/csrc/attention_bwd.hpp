@@ -14,7 +14,8 @@
 // score products start from. dK = ln(2) * dS^T Qs.
 //
 // Two kernels, no atomics (deterministic):
-//   * attn_bwd_dkdv_kernel: one workgroup per (group, sequence, 128 keys);
+//   * attn_bwd_dkdv_kernel: one workgroup per (group, sequence, 256 keys at
+//     d = 64, 128 at d = 32);
 //     each wave keeps 32 keys' K and V as resident MFMA operands and
 //     accumulates their dK^T, dV^T over every query row at or after the
 //     keys, 64 rows per step staged in LDS (Q, dO row-major for the score
@@ -65,12 +66,16 @@ struct AttnBwdArgs {
 // their LDS at 48 KB, 32-key sub-steps their registers at 168): the waves
 // sharing a SIMD then come from independent workgroups and overlap one
 // another's exponent and product phases (10% faster than one eight-wave
-// workgroup of 128-key tiles per CU at T = 32K).
+// workgroup of 128-key tiles per CU at T = 32K). The dK/dV kernel at d = 64
+// runs one eight-wave workgroup of 256 keys per CU: each staged Q/dO step
+// then serves twice the keys, which halves the staged traffic (T = 1M:
+// 4.25 -> 3.42 s, where the query rows no longer stay in L2; 1-2.5% at
+// 16K-32K; 3% slower on the 0.12 ms kernel at T = 2048).
 #ifndef GQE_BWD_KW
 #define GQE_BWD_KW 32
 #endif
 #ifndef GQE_BWD_NW
-#define GQE_BWD_NW 4
+#define GQE_BWD_NW 8
 #endif
 #ifndef GQE_BWD_RS
 #define GQE_BWD_RS 64
