@@ -54,7 +54,7 @@ using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
 
 // Sequence padding of the K / V^T buffers: whole key tiles of the forward
 // and whole key blocks of the dK/dV kernel (its waves read their keys' rows).
-constexpr int kKVPad = std::max({AttnShort::BKV, AttnLong::BKV, kBwdBKMax});
+constexpr int kKVPad = std::max({AttnShort::BKV, AttnLong::BKV, kBwdBKMax, kBwdBKVMax});
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -373,7 +373,7 @@ struct TrainWs {
     size_t lse, dlt, Qc, Qt, dOc, dOt, dw, dz, p, cs, dC, WoT, WcT, xT, doT, CT, Kt, V, dY, dYt, part, total;
 };
 
-constexpr int kRowPad = kBwdDqBQ > 256 ? kBwdDqBQ : 256;   // row-space runs pad to whole dQ row tiles
+constexpr int kRowPad = kBwdDqBQMax > 256 ? kBwdDqBQMax : 256;   // row-space runs pad to whole dQ row tiles
 constexpr int kColsumRows = 256;
 
 // Splits of a weight-gradient GEMM over its token contraction: about 1024
@@ -627,10 +627,14 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
     }
     mk.at(4);
     {
-        ab.n_tiles = (int)((d.T * (d.k + 1) + kBwdDqBQ - 1) / kBwdDqBQ);
+        // Long sequences (d = 64) take the 256-row shape, as the forward does.
+        const bool lng = d.d == 64 && d.T > kAttnLongT;
+        const int bq = lng ? DqLong::BQ : DqShort::BQ;
+        ab.n_tiles = (int)((d.T * (d.k + 1) + bq - 1) / bq);
         const dim3 grid((unsigned)((int64_t)ab.n_tiles * d.G * d.B));
-        if (d.d == 64) hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(kBwdDqNW * 64), 0, st, ab);
-        else hipLaunchKernelGGL(attn_bwd_dq_kernel<32>, grid, dim3(kBwdDqNW * 64), 0, st, ab);
+        if (lng) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, DqLong>), grid, dim3(DqLong::NW * 64), 0, st, ab);
+        else if (d.d == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, DqShort>), grid, dim3(DqShort::NW * 64), 0, st, ab);
+        else hipLaunchKernelGGL((attn_bwd_dq_kernel<32, DqShort>), grid, dim3(DqShort::NW * 64), 0, st, ab);
     }
     mk.at(5);
 

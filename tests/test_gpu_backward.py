@@ -151,3 +151,35 @@ def test_backward_properties_at_32k():
         assert np.isfinite(a[k]).all(), k
         assert np.array_equal(a[k], b[k]), (k, "rerun differs")
         assert np.array_equal(2 * a[k], c[k]), (k, "not linear in dout")
+
+
+def test_backward_long_shape_against_its_prefix():
+    """Past 256K tokens (d = 64) the dQ kernel takes its long shape (eight
+    waves, 256 rows, 128-key tiles), far beyond what the fp64 oracle runs.
+    Causality gives an exact check: with dout zero after the first P tokens
+    and no balancing loss (which couples all tokens), every gradient of the
+    long sequence equals that of its P-token prefix run on its own, which takes
+    the short shapes checked against the oracle above. A token's dQ reads only
+    keys up to it; its dK, dV read only queries from it on, whose dO is zero
+    past P; the weight gradients sum over rows whose gradients vanish past P.
+    The runs differ only in rounding order (long and short forward tiles,
+    split-K sums over more rows), so the bar is the parity bar, and dx past P
+    must be zero up to fp32 rounding."""
+    P = 2048
+    s_long = Shape(B=1, T=262144 + 64, D=128, G=2, M=2, k=1, d=64)
+    s_pre = Shape(B=1, T=P, D=128, G=2, M=2, k=1, d=64)
+    print(f"[backward long shape vs prefix] {s_long}", flush=True)
+    inp = make_inputs(s_long, seed=71)
+    dout = make_grad_output(s_long, seed=72)
+    dout[P:] = 0
+    long_res = run_train(s_long, H.to_device(inp), dout.cuda(), 0.0)
+    pre_inp = dict(inp)
+    pre_inp["x"] = inp["x"][:P].clone()
+    pre_res = run_train(s_pre, H.to_device(pre_inp), dout[:P].clone().cuda(), 0.0)
+    assert (long_res["idx"][:P] == pre_res["idx"]).all(), "routing of the prefix"
+    scale = max(float(np.abs(pre_res[k]).max()) for k in GRADS)
+    for k in GRADS:
+        got = long_res[k][:P] if k == "dx" else long_res[k]
+        compare("long_vs_prefix", k, got, pre_res[k], scale)
+    assert np.isfinite(long_res["dx"]).all()
+    assert float(np.abs(long_res["dx"][P:]).max()) <= ZERO_REL * scale, "dx past the prefix"
