@@ -69,7 +69,11 @@ typedef enum {
     GQE_ERR_UNSUPPORTED = -3,  /* a valid size the library does not handle (d_h, D, M, G*M) */
     GQE_ERR_WORKSPACE = -4,    /* ws_bytes smaller than the *_workspace_bytes figure */
     GQE_ERR_ALIGN = -5,        /* a pointer not aligned to 16 bytes */
-    GQE_ERR_HIP = -6           /* the HIP runtime reported an error at launch */
+    GQE_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
+    /* Not a status: widens the enum's value range to all of int32, so that
+     * gqe_status_str may be handed any int (C++ leaves reading an enum value
+     * outside its range undefined). */
+    GQE_STATUS_RANGE_ = 0x7fffffff
 } gqe_status;
 
 typedef enum { GQE_BF16 = 0, GQE_F32 = 1 } gqe_dtype;

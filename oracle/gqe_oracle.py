@@ -215,14 +215,30 @@ def _routed_queries(x: np.ndarray, Wq: np.ndarray, sel: np.ndarray) -> np.ndarra
     return Qr
 
 
+def _map_heads(fn, jobs, workers: int):
+    """[fn(*job) for job in jobs], on a pool of `workers` threads when workers > 1.
+
+    The heads are independent computations and each one runs the same numpy
+    calls either way, so the results are bit-identical to the serial loop; the
+    threads only let several heads' large array operations (which release the
+    interpreter lock) run at once on the big layers."""
+    if workers <= 1 or len(jobs) <= 1:
+        return [fn(*j) for j in jobs]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(lambda j: fn(*j), jobs))
+
+
 def gqe_forward(inp: dict, G: int, M: int, k: int, d: int, B: int, T: int,
-                shared_kv_group: int = 0, q_block: int = 512, variant: str = "full") -> dict:
+                shared_kv_group: int = 0, q_block: int = 512, variant: str = "full",
+                workers: int = 1) -> dict:
     """The whole GQE layer in fp64. inp holds float64 arrays x, Wr, br (or None),
     Wq [G*M*d,D], Wk [G*d,D], Wv [G*d,D], Wq_sh [d,D], Wo [D, variant_slots*d].
 
     Expert e = g*M + m owns rows e*d .. e*d+d-1 of Wq. The returned w is the
     weight the variant applies to each pick: p_pick for the weighted
-    concatenation, the renormalised w otherwise.
+    concatenation, the renormalised w otherwise. workers > 1 runs the
+    per-head attentions on that many threads (same results).
     """
     x = inp["x"]
     N = x.shape[0]
@@ -236,15 +252,17 @@ def gqe_forward(inp: dict, G: int, M: int, k: int, d: int, B: int, T: int,
     Qr = _routed_queries(x, Wq, sel)
     Q_sh = project(x, inp["Wq_sh"])
 
+    # One attention per routed (g, r) head slot, then the shared head.
+    jobs = [(Qr[:, g, r].reshape(B, T, d), K[:, :, g], V[:, :, g], q_block) for g in range(G) for r in range(k)]
+    s0 = shared_kv_group
+    if variant != "no_shared":
+        jobs.append((Q_sh.reshape(B, T, d), K[:, :, s0], V[:, :, s0], q_block))
+    res = _map_heads(causal_attention, jobs, workers)
     O = np.empty((N, G, k, d))
     for g in range(G):
         for r in range(k):
-            q = Qr[:, g, r].reshape(B, T, d)
-            O[:, g, r] = causal_attention(q, K[:, :, g], V[:, :, g], q_block).reshape(N, d)
-    s0 = shared_kv_group
-    O_sh = None
-    if variant != "no_shared":
-        O_sh = causal_attention(Q_sh.reshape(B, T, d), K[:, :, s0], V[:, :, s0], q_block).reshape(N, d)
+            O[:, g, r] = res[g * k + r].reshape(N, d)
+    O_sh = res[G * k].reshape(N, d) if variant != "no_shared" else None
 
     p_pick = pick_probs(p, sel)
     C = assemble_variant(O, w, p_pick, O_sh, variant)
@@ -253,11 +271,12 @@ def gqe_forward(inp: dict, G: int, M: int, k: int, d: int, B: int, T: int,
                 Q_sh=Q_sh, K=K.reshape(N, G, d), V=V.reshape(N, G, d), C=C, out=out)
 
 
-def gqa_forward(inp: dict, G: int, Hq: int, d: int, B: int, T: int, q_block: int = 512) -> dict:
+def gqa_forward(inp: dict, G: int, Hq: int, d: int, B: int, T: int, q_block: int = 512,
+                workers: int = 1) -> dict:
     """Dense GQA: every query head on every token, head h on KV group h // (Hq/G).
 
     [GQA-w] "Mechanism": query heads split into groups sharing one K/V head.
-    inp: x, Wq [Hq*d,D], Wk, Wv [G*d,D], Wo [D,Hq*d].
+    inp: x, Wq [Hq*d,D], Wk, Wv [G*d,D], Wo [D,Hq*d]. workers as in gqe_forward.
     """
     x = inp["x"]
     N = x.shape[0]
@@ -265,10 +284,11 @@ def gqa_forward(inp: dict, G: int, Hq: int, d: int, B: int, T: int, q_block: int
     Q = project(x, inp["Wq"]).reshape(B, T, Hq, d)
     K = project(x, inp["Wk"]).reshape(B, T, G, d)
     V = project(x, inp["Wv"]).reshape(B, T, G, d)
+    res = _map_heads(causal_attention, [(Q[:, :, h], K[:, :, h // per], V[:, :, h // per], q_block)
+                                        for h in range(Hq)], workers)
     O = np.empty((N, Hq, d))
     for h in range(Hq):
-        g = h // per
-        O[:, h] = causal_attention(Q[:, :, h], K[:, :, g], V[:, :, g], q_block).reshape(N, d)
+        O[:, h] = res[h].reshape(N, d)
     C = O.reshape(N, Hq * d)
     return dict(Q=Q.reshape(N, Hq, d), C=C, out=project(C, inp["Wo"]))
 

@@ -24,7 +24,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgqe.so")
+# GQE_LIB_PATH selects another build of the same library (the host-sanitizer
+# build the ABI tests also run against); the default is the in-tree libgqe.so.
+LIB_PATH = os.environ.get("GQE_LIB_PATH") or os.path.join(HERE, "libgqe.so")
 
 GQE_BF16, GQE_F32 = 0, 1
 # Merge variants (gqe_variant): the layer and the pages' three ablations.

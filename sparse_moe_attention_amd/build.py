@@ -50,6 +50,47 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+# Host-side sanitizers: AddressSanitizer and UndefinedBehaviorSanitizer on the
+# host pass only (each -fsanitize= behind -Xarch_host); the device code is
+# built as usual and never runs on the CPU. Used by the CPU tests, which run
+# every argument-checking path of the C ABI against this build.
+SAN_OUT = os.path.join(HERE, "_build", "libgqe_hostsan.so")
+SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g",
+    # every uninitialised local holds a 0xAA.. pattern instead of whatever the
+    # stack held, so a read of one changes the checks' results every time
+    "-Xarch_host", "-ftrivial-auto-var-init=pattern",
+]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libgqe with ASan + UBSan in its host code, at SAN_OUT; returns the path."""
+    os.makedirs(os.path.dirname(SAN_OUT), exist_ok=True)
+    tmp = SAN_OUT + f".tmp{os.getpid()}"
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1"] + SAN_FLAGS
+    cmd = [hipcc_path(), *flags, "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc (host sanitizers) failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, SAN_OUT)
+    return SAN_OUT
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime that a non-instrumented host (python) must preload."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc_path())), "..", "llvm", "bin", "clang")
+    for c in (clang, "/opt/rocm/llvm/bin/clang", shutil.which("clang") or ""):
+        if c and os.path.exists(c):
+            res = subprocess.run([c, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            path = res.stdout.strip()
+            if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    raise RuntimeError("clang's ASan runtime (libclang_rt.asan-x86_64.so) not found")
+
+
 def undefined_kernel_stubs(lib: str) -> list[str]:
     """Kernel launch stubs the library references but does not define.
 

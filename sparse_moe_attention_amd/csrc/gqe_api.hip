@@ -972,9 +972,10 @@ static gqe_status check_gqa(int64_t B, int64_t T, int64_t D, int32_t Hq, int32_t
                             Dims* o) {
     if (B < 1 || T < 1 || D < 1 || Hq < 1 || G < 1) return GQE_ERR_SHAPE;
     if (Hq % G != 0 || Hq > 256) return GQE_ERR_SHAPE;
-    gqe_shape s;
+    gqe_shape s{};
     s.B = B; s.T = T; s.D = D; s.G = G; s.M = Hq / G; s.k = Hq / G; s.d_h = d_h;
     s.shared_kv_group = 0; s.dtype = dtype;
+    s.variant = GQE_FULL;
     return check_shape(&s, o);
 }
 
@@ -1059,6 +1060,7 @@ const char* gqe_status_str(gqe_status st) {
         case GQE_ERR_WORKSPACE: return "GQE_ERR_WORKSPACE: workspace smaller than required";
         case GQE_ERR_ALIGN: return "GQE_ERR_ALIGN: a pointer is not 16-byte aligned";
         case GQE_ERR_HIP: return "GQE_ERR_HIP: the HIP runtime reported an error";
+        default: break;
     }
     return "unknown gqe_status";
 }

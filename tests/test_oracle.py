@@ -389,7 +389,24 @@ def pin_variants_against_full():
             assert (pp > 0).all() and (pp <= 1).all()
 
 
+def pin_threaded_heads_identical():
+    """workers > 1 (heads on a thread pool, used for the large layers) returns
+    bit-identical arrays to the serial loop, for GQE (k = 2, shared head on
+    group 1, ragged query blocks) and for dense GQA."""
+    rng = np.random.default_rng(29)
+    B, T, D, G, M, k, d = 2, 45, 32, 3, 3, 2, 8
+    inp = rand_layer(rng, B, T, D, G, M, k, d, bias=True)
+    a = go.gqe_forward(inp, G, M, k, d, B, T, shared_kv_group=1, q_block=16)
+    b = go.gqe_forward(inp, G, M, k, d, B, T, shared_kv_group=1, q_block=16, workers=4)
+    for key in ("C", "out", "Qr", "w"):
+        assert np.array_equal(a[key], b[key]), key
+    ga = dict(x=inp["x"], Wq=inp["Wq"], Wk=inp["Wk"], Wv=inp["Wv"], Wo=inp["Wo_gqa"])
+    assert np.array_equal(go.gqa_forward(ga, G, G * M, d, B, T, q_block=16)["out"],
+                          go.gqa_forward(ga, G, G * M, d, B, T, q_block=16, workers=5)["out"])
+
+
 PINS = [
+    pin_threaded_heads_identical,
     pin_topk_brute_force, pin_group_softmax_scipy, pin_route_tiny_brute_force,
     pin_route_uniform_router, pin_route_single_expert, pin_route_invariants,
     pin_attention_brute_force, pin_attention_sdpa, pin_attention_closed_forms,
