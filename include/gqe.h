@@ -70,6 +70,8 @@ typedef enum {
     GQE_ERR_WORKSPACE = -4,    /* ws_bytes smaller than the *_workspace_bytes figure */
     GQE_ERR_ALIGN = -5,        /* a pointer not aligned to 16 bytes */
     GQE_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
+    GQE_ERR_SCRATCH = -7,      /* gqe_attn_fwd_noalloc: the shape's workspace exceeds
+                                  GQE_NOALLOC_SCRATCH_BYTES */
     /* Not a status: widens the enum's value range to all of int32, so that
      * gqe_status_str may be handed any int (C++ leaves reading an enum value
      * outside its range undefined). */
@@ -162,6 +164,28 @@ gqe_status gqe_attn_fwd(const gqe_shape* s, const void* x, const void* Wr, const
                         const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh,
                         const void* Wo, void* out, int32_t* idx_out, float* w_out,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* gqe_attn_fwd without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and kernels as gqe_attn_fwd,
+ * minus ws / ws_bytes: the workspace is a static device array of
+ * GQE_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends. The call allocates and frees nothing.
+ *   - Shapes whose gqe_workspace_bytes exceeds GQE_NOALLOC_SCRATCH_BYTES
+ *     return GQE_ERR_SCRATCH before any HIP call (256 MiB holds the B1 T32768
+ *     D1024 G8 M2 k1 layer's 150 MB and the B2 T16384 D2048 G8 M4 k2 layer's
+ *     225 MB; the 1M-token layer needs the workspace form).
+ *   - Every call on a device shares that device's array, and it keeps the
+ *     last call's contents (the forward needs none of them cleared). Calls
+ *     that overlap on one device, on any streams or threads, race on it:
+ *     the caller must order them (one stream, or events between streams).
+ *   - Errors as for gqe_attn_fwd, plus GQE_ERR_SCRATCH; GQE_ERR_HIP also if
+ *     the array's device address cannot be looked up. */
+#define GQE_NOALLOC_SCRATCH_BYTES (256ull << 20)
+gqe_status gqe_attn_fwd_noalloc(const gqe_shape* s, const void* x, const void* Wr, const float* br,
+                                const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh,
+                                const void* Wo, void* out, int32_t* idx_out, float* w_out,
+                                void* stream);
 
 /* Dense GQA baseline over the same kernels: Hq query heads, G KV groups, head
  * h reads group h / (Hq/G), every head active on every token.

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI in include/gqe.h):
     gqe_route(shape, x, Wr, br, idx, w, logits=None, counts=None, ws=None)
     gqe_attn_fwd_routed(shape, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, slots_out=None, ws=None)
     gqe_attn_fwd(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out=None, w_out=None, ws=None)
+    gqe_attn_fwd_noalloc(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out=None, w_out=None)
     gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype)
     gqa_attn_fwd(B, T, D, Hq, G, d_h, dtype, x, Wq, Wk, Wv, Wo, out, ws=None)
     gqe_train_workspace_bytes(shape)
@@ -34,6 +35,7 @@ GQE_FULL, GQE_WEIGHTED_CONCAT, GQE_HARD_CONCAT, GQE_NO_SHARED = 0, 1, 2, 3
 VARIANT_CODES = {"full": GQE_FULL, "weighted_concat": GQE_WEIGHTED_CONCAT, "hard_concat": GQE_HARD_CONCAT,
                  "no_shared": GQE_NO_SHARED}
 GQE_N_STAGES, GQA_N_STAGES = 8, 3
+GQE_NOALLOC_SCRATCH_BYTES = 256 << 20     # static scratch of gqe_attn_fwd_noalloc (include/gqe.h)
 GQE_STAGE_NAMES = ("proj_kv_qsh_router", "route", "scan", "scatter", "grouped_q", "attention",
                    "weighted_slot", "out_proj")
 GQA_STAGE_NAMES = ("proj_qkv", "attention", "out_proj")
@@ -47,7 +49,7 @@ BWD_GRADS = ("dx", "dWr", "dWq", "dWk", "dWv", "dWq_sh", "dWo")
 
 STATUS = {
     0: "GQE_OK", -1: "GQE_ERR_NULL", -2: "GQE_ERR_SHAPE", -3: "GQE_ERR_UNSUPPORTED",
-    -4: "GQE_ERR_WORKSPACE", -5: "GQE_ERR_ALIGN", -6: "GQE_ERR_HIP",
+    -4: "GQE_ERR_WORKSPACE", -5: "GQE_ERR_ALIGN", -6: "GQE_ERR_HIP", -7: "GQE_ERR_SCRATCH",
 }
 
 
@@ -90,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.gqe_attn_fwd_routed.restype = ctypes.c_int
     lib.gqe_attn_fwd.argtypes = [SH, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gqe_attn_fwd.restype = ctypes.c_int
+    lib.gqe_attn_fwd_noalloc.argtypes = [SH, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gqe_attn_fwd_noalloc.restype = ctypes.c_int
     lib.gqa_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, I32, I32]
     lib.gqa_workspace_bytes.restype = S
     lib.gqa_attn_fwd.argtypes = [I64, I64, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, S, P]
@@ -194,6 +198,14 @@ def gqe_attn_fwd(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out=None, w_o
     _check(lib.gqe_attn_fwd(ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(br), _ptr(Wq), _ptr(Wk), _ptr(Wv),
                             _ptr(Wq_sh), _ptr(Wo), _ptr(out), _ptr(idx_out), _ptr(w_out), _ptr(ws),
                             ws.numel(), _stream(stream)))
+
+
+def gqe_attn_fwd_noalloc(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out=None, w_out=None, stream=None):
+    """gqe_attn_fwd on the library's static device scratch (no workspace, no
+    allocation); shapes needing more than GQE_NOALLOC_SCRATCH_BYTES raise."""
+    _check(load().gqe_attn_fwd_noalloc(ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(br), _ptr(Wq), _ptr(Wk),
+                                       _ptr(Wv), _ptr(Wq_sh), _ptr(Wo), _ptr(out), _ptr(idx_out), _ptr(w_out),
+                                       _stream(stream)))
 
 
 def gqa_workspace_bytes(B, T, D, Hq, G, d_h, dtype=GQE_BF16) -> int:

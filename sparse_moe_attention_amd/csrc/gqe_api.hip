@@ -19,6 +19,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gqe.h"
 #include "attention.hpp"
@@ -847,6 +848,39 @@ gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, co
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace lives in a static device array.
+// ---------------------------------------------------------------------------
+// Each device the library runs on holds its own copy of `scratch` from the
+// code object's load until the process ends. Host code must never pass the
+// array's name to a kernel or a copy (on the host it is only a stand-in for
+// the symbol): scratch_base() looks up this device's address once and every
+// launch takes that pointer.
+static __device__ __align__(256) char scratch[GQE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_base[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+gqe_status scratch_base(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_base[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GQE_ERR_HIP;
+        g_scratch_base[dev] = p;
+    }
+    *out = g_scratch_base[dev];
+    return GQE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t gqe_workspace_bytes(const gqe_shape* s) {
@@ -912,6 +946,28 @@ gqe_status gqe_attn_fwd(const gqe_shape* s, const void* x, const void* Wr, const
                         int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
     return gqe_attn_fwd_timed(s, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out, w_out, ws, ws_bytes, stream,
                               nullptr);
+}
+
+gqe_status gqe_attn_fwd_noalloc(const gqe_shape* s, const void* x, const void* Wr, const float* br,
+                                const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo,
+                                void* out, int32_t* idx_out, float* w_out, void* stream) {
+    // Every argument check of gqe_attn_fwd, and the scratch bound, before any HIP call.
+    Dims d;
+    gqe_status rc = check_shape(s, &d);
+    if (rc != GQE_OK) return rc;
+    if (!x || !Wr || !Wq || !Wk || !Wv || !Wq_sh || !Wo || !out) return GQE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(Wr) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
+        !aligned16(Wq_sh) || !aligned16(Wo) || !aligned16(out) || (br && !aligned16(br)) ||
+        (idx_out && !aligned16(idx_out)) || (w_out && !aligned16(w_out)))
+        return GQE_ERR_ALIGN;
+    if (gqe_layout(d).total > (size_t)GQE_NOALLOC_SCRATCH_BYTES) return GQE_ERR_SCRATCH;
+    void* ws = nullptr;
+    if ((rc = scratch_base(&ws)) != GQE_OK) return rc;
+    // The forward writes every workspace entry it reads (K/V rows past T are
+    // masked, V^T columns past T zeroed in LDS), so the previous call's
+    // contents need no clearing.
+    return fwd_impl(s, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out, w_out, ws, (size_t)GQE_NOALLOC_SCRATCH_BYTES,
+                    stream, nullptr, false);
 }
 
 size_t gqe_train_workspace_bytes(const gqe_shape* s) {
@@ -1060,6 +1116,7 @@ const char* gqe_status_str(gqe_status st) {
         case GQE_ERR_WORKSPACE: return "GQE_ERR_WORKSPACE: workspace smaller than required";
         case GQE_ERR_ALIGN: return "GQE_ERR_ALIGN: a pointer is not 16-byte aligned";
         case GQE_ERR_HIP: return "GQE_ERR_HIP: the HIP runtime reported an error";
+        case GQE_ERR_SCRATCH: return "GQE_ERR_SCRATCH: the shape needs more workspace than the static scratch holds";
         default: break;
     }
     return "unknown gqe_status";

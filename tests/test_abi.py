@@ -194,3 +194,29 @@ def test_decode_shape_errors(lib):
         rc = lib.gqe_decode_step(ctypes.byref(bad), A, A, A, None, A, A, A, A, A, A, A, A, None, None, A,
                                  1 << 40, None)
         assert rc == -2
+
+
+def test_noalloc_entry_point_validates(lib):
+    """gqe_attn_fwd_noalloc: the checks of gqe_attn_fwd, plus the static
+    scratch bound (GQE_ERR_SCRATCH), all before any HIP call."""
+    s = shape()
+
+    def call(sh, **o):
+        return lib.gqe_attn_fwd_noalloc(ctypes.byref(sh) if sh is not None else None, o.get("x", A), A,
+                                        o.get("br"), A, A, A, A, A, o.get("out", A), o.get("idx"), o.get("w"), None)
+
+    assert call(None) == -1
+    assert call(shape(k=3)) == -2
+    assert call(shape(d_h=48)) == -3
+    assert call(s, x=None) == -1
+    assert call(s, out=None) == -1
+    assert call(s, out=BAD) == -5
+    assert call(s, br=BAD) == -5
+    assert call(s, idx=BAD) == -5
+    huge = shape(T=1 << 20, D=1024, G=8, M=2, d_h=64)
+    assert lib.gqe_workspace_bytes(ctypes.byref(huge)) > gq.GQE_NOALLOC_SCRATCH_BYTES
+    assert call(huge) == -7
+    assert gq.gqe_status_str(-7).startswith("GQE_ERR_SCRATCH")
+    # the 32K-token layer and the larger-pool layer fit the scratch
+    for sh in (shape(T=32768, D=1024, G=8, M=2, d_h=64), shape(B=2, T=16384, D=2048, G=8, M=4, k=2, d_h=64)):
+        assert 0 < lib.gqe_workspace_bytes(ctypes.byref(sh)) <= gq.GQE_NOALLOC_SCRATCH_BYTES
