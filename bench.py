@@ -60,6 +60,114 @@ def attn_bwd_flops(s, heads: int) -> float:
     return 2.5 * attn_flops(s, heads)
 
 
+def layer_leg(gq, torch, s, dv, steps, warmup, mk_events, with_gqa=True):
+    """gqe_attn_fwd on one workload: W warmup steps, then K timed steps with
+    HIP events around the attention kernel in every step (on the library's
+    stream), one extra isolated step for the per-stage breakdown, and the dense
+    GQA layer (all G*M heads) on the same tensors."""
+    dt = s.torch_dtype()
+    shape = gq.shape_from(s)
+    out = torch.empty(s.N, s.D, dtype=dt, device="cuda")
+    ws = torch.empty(gq.gqe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    dcode = gq.GQE_F32 if s.dtype == "f32" else gq.GQE_BF16
+    A0, A1 = 5, 6                    # events before / after the attention stage
+
+    def fwd(arr=None):
+        gq.gqe_attn_fwd_timed(shape, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"],
+                              dv["Wo"], out, arr, ws=ws)
+
+    for _ in range(warmup):
+        fwd()
+    step_ev = []
+    for _ in range(steps):
+        e = mk_events(2)
+        arr = [None] * (gq.GQE_N_STAGES + 1)
+        arr[A0], arr[A1] = e
+        step_ev.append((e, gq.event_array(arr)))
+    t0, t1 = mk_events(2)
+    torch.cuda.synchronize()
+    wall = time.perf_counter()
+    t0.record()
+    for _, arr in step_ev:
+        fwd(arr)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    ms_step = t0.elapsed_time(t1) / steps
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e, _ in step_ev) / steps
+
+    # one fully instrumented step for the per-stage breakdown (outside the timed region)
+    evs = mk_events(gq.GQE_N_STAGES + 1)
+    torch.cuda.synchronize()
+    fwd(gq.event_array(evs))
+    torch.cuda.synchronize()
+    stage_ms = {n: round(evs[i].elapsed_time(evs[i + 1]), 4) for i, n in enumerate(gq.GQE_STAGE_NAMES)}
+    del ws, out
+
+    gqa = None
+    if with_gqa:
+        wsg = torch.empty(gq.gqa_workspace_bytes(s.B, s.T, s.D, s.Hq, s.G, s.d, dcode), dtype=torch.uint8,
+                          device="cuda")
+        og = torch.empty(s.N, s.D, dtype=dt, device="cuda")
+
+        def gfwd(arr=None):
+            gq.gqa_attn_fwd_timed(s.B, s.T, s.D, s.Hq, s.G, s.d, dcode, dv["x"], dv["Wq"], dv["Wk"], dv["Wv"],
+                                  dv["Wo_gqa"], og, arr, ws=wsg)
+
+        for _ in range(warmup):
+            gfwd()
+        gev = []
+        for _ in range(steps):
+            e = mk_events(2)
+            arr = [None] * (gq.GQA_N_STAGES + 1)
+            arr[1], arr[2] = e
+            gev.append((e, gq.event_array(arr)))
+        g0, g1 = mk_events(2)
+        torch.cuda.synchronize()
+        g0.record()
+        for _, arr in gev:
+            gfwd(arr)
+        g1.record()
+        torch.cuda.synchronize()
+        gqa_ms = g0.elapsed_time(g1) / steps
+        gqa_attn_ms = sum(e[0].elapsed_time(e[1]) for e, _ in gev) / steps
+        gqa = {"tokens_per_s": s.N / (gqa_ms / 1e3), "ms_per_step": gqa_ms, "attention_ms": gqa_attn_ms,
+               "heads": f"{s.Hq}q/{s.G}kv", "speedup_gqe_over_gqa": gqa_ms / ms_step,
+               "attention_speedup": gqa_attn_ms / attn_ms}
+        del wsg, og
+    peak = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
+    fl = attn_flops(s, active_heads(s))
+    achieved = fl / (attn_ms / 1e3) / 1e12
+    return {"tokens_per_s": s.N / (ms_step / 1e3), "ms_per_step": ms_step, "steps": steps, "warmup": warmup,
+            "attention_ms": attn_ms, "attn_tflops": achieved, "attn_frac": achieved / peak,
+            "layer_mfma_frac": layer_flops(s) / (ms_step / 1e3) / 1e12 / peak, "stage_ms": stage_ms,
+            "gqa_baseline": gqa, "wall_s_timed_region": wall}
+
+
+OTHER_STEPS = {1: 50, 2: 50, 3: 20, 4: 20, 5: 3}
+
+
+def other_configs(gq, torch, headline: int, warmup: int, mk_events):
+    """The other workloads at one GPU, each timed like the headline (fewer steps
+    at 1M tokens); reported beside the headline, never as its value."""
+    from workloads import CONFIG_NAMES, config_inputs
+    res = {}
+    for cid in sorted(OTHER_STEPS):
+        if cid == headline:
+            continue
+        s, inp = config_inputs(cid)
+        dv = {k: (v.cuda().contiguous() if v is not None else None) for k, v in inp.items()}
+        del inp
+        r = layer_leg(gq, torch, s, dv, OTHER_STEPS[cid], min(warmup, 1) if cid == 5 else warmup, mk_events)
+        r["workload"] = CONFIG_NAMES[cid]
+        res[f"config{cid}"] = r
+        del dv
+        torch.cuda.empty_cache()
+        print(f"[bench] config {cid}: {r['tokens_per_s']:.4g} tokens/s, attention frac {r['attn_frac']:.3f}",
+              file=sys.stderr, flush=True)
+    return res
+
+
 def train_leg(gq, torch, s, dv, steps, warmup, mk_events):
     """Training step = gqe_attn_fwd_train + gqe_attn_bwd on the same inputs
     (dout seeded, resident in HBM). Returns the record's "backward" object."""
@@ -199,6 +307,12 @@ def cpu_baseline(s, inp, target_s: float):
         cores = max(int(p.get("num_threads", 1)) for p in threadpool_info()) if threadpool_info() else 1
     except Exception:
         cores = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next(ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     f = {k: to_f64(v) for k, v in inp.items()}
     t = time.perf_counter()
     go.route(f["x"], f["Wr"], f.get("br"), s.G, s.M, s.k)
@@ -218,7 +332,8 @@ def cpu_baseline(s, inp, target_s: float):
     per_row = max((t_rows - t_fixed) / len(rows), 1e-9)
     est = t_fixed + s.N * per_row
     return {
-        "value": s.N / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "value": s.N / est, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model,
+        "host_cpus_visible": os.cpu_count(),
         "sample": (f"fp64 numpy oracle: routing + K/V projection of all {s.N} tokens in full "
                    f"({t_fixed:.2f} s), then {len(rows)} stratified rows of the full layer over their whole "
                    f"causal prefix ({t_rows:.2f} s incl. the dense part again), per-row cost scaled to N; "
@@ -237,6 +352,8 @@ def main():
     ap.add_argument("--no-gqa", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the training-step (forward + backward) leg")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other workloads (reported under \"configs\")")
     ap.add_argument("--variant", default="full", choices=["full", "weighted_concat", "hard_concat", "no_shared"],
                     help="merge of the picked experts: the layer, or one of the pages' ablations")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -271,78 +388,15 @@ def main():
         inp = dict(inp, Wo=inp["Wo"][:, :s.slots * s.d].contiguous())
     steps = args.steps if args.steps is not None else {1: 50, 2: 50, 3: 20, 4: 20, 5: 3}[args.config]
     dv = {k: (v.cuda().contiguous() if v is not None else None) for k, v in inp.items()}
-    dt = s.torch_dtype()
-    shape = gq.shape_from(s)
-    out = torch.empty(s.N, s.D, dtype=dt, device="cuda")
-    ws = torch.empty(gq.gqe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
-    dcode = gq.GQE_F32 if s.dtype == "f32" else gq.GQE_BF16
-
     def mk_events(n):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for e in evs:
             e.record()
         return evs
 
-    # ---- GQE: warmup, then K timed steps; events bracket the attention kernel
-    A0, A1 = 5, 6                    # events before / after the attention stage
-    for _ in range(args.warmup):
-        gq.gqe_attn_fwd(shape, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"],
-                        dv["Wo"], out, ws=ws)
-    step_ev = []
-    for _ in range(steps):
-        e = mk_events(2)
-        arr = [None] * (gq.GQE_N_STAGES + 1)
-        arr[A0], arr[A1] = e
-        step_ev.append((e, gq.event_array(arr)))
-    t0, t1 = mk_events(2)
-    torch.cuda.synchronize()
-    wall = time.perf_counter()
-    t0.record()
-    for _, arr in step_ev:
-        gq.gqe_attn_fwd_timed(shape, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"],
-                              dv["Wo"], out, arr, ws=ws)
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall
-    ms_step = t0.elapsed_time(t1) / steps
-    attn_ms = sum(e[0].elapsed_time(e[1]) for e, _ in step_ev) / steps
-
-    # one fully instrumented step for the per-stage breakdown (outside the timed region)
-    evs = mk_events(gq.GQE_N_STAGES + 1)
-    torch.cuda.synchronize()
-    gq.gqe_attn_fwd_timed(shape, dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"], dv["Wq_sh"],
-                          dv["Wo"], out, gq.event_array(evs), ws=ws)
-    torch.cuda.synchronize()
-    stage_ms = {n: round(evs[i].elapsed_time(evs[i + 1]), 4) for i, n in enumerate(gq.GQE_STAGE_NAMES)}
-
-    # ---- dense GQA over the same tensors
-    gqa = None
-    if not args.no_gqa:
-        wsg = torch.empty(gq.gqa_workspace_bytes(s.B, s.T, s.D, s.Hq, s.G, s.d, dcode), dtype=torch.uint8,
-                          device="cuda")
-        og = torch.empty_like(out)
-        for _ in range(args.warmup):
-            gq.gqa_attn_fwd(s.B, s.T, s.D, s.Hq, s.G, s.d, dcode, dv["x"], dv["Wq"], dv["Wk"], dv["Wv"],
-                            dv["Wo_gqa"], og, ws=wsg)
-        gev = []
-        for _ in range(steps):
-            e = mk_events(2)
-            arr = [None] * (gq.GQA_N_STAGES + 1)
-            arr[1], arr[2] = e
-            gev.append((e, gq.event_array(arr)))
-        g0, g1 = mk_events(2)
-        torch.cuda.synchronize()
-        g0.record()
-        for _, arr in gev:
-            gq.gqa_attn_fwd_timed(s.B, s.T, s.D, s.Hq, s.G, s.d, dcode, dv["x"], dv["Wq"], dv["Wk"], dv["Wv"],
-                                  dv["Wo_gqa"], og, arr, ws=wsg)
-        g1.record()
-        torch.cuda.synchronize()
-        gqa_ms = g0.elapsed_time(g1) / steps
-        gqa_attn_ms = sum(e[0].elapsed_time(e[1]) for e, _ in gev) / steps
-        gqa = {"tokens_per_s": s.N / (gqa_ms / 1e3), "ms_per_step": gqa_ms, "attention_ms": gqa_attn_ms,
-               "heads": f"{s.Hq}q/{s.G}kv", "speedup_gqe_over_gqa": gqa_ms / ms_step,
-               "attention_speedup": gqa_attn_ms / attn_ms}
+    lay = layer_leg(gq, torch, s, dv, steps, args.warmup, mk_events, with_gqa=not args.no_gqa)
+    ms_step, attn_ms, wall = lay["ms_per_step"], lay["attention_ms"], lay["wall_s_timed_region"]
+    stage_ms, gqa = lay["stage_ms"], lay["gqa_baseline"]
 
     bwd = None
     if not args.no_backward and s.dtype == "bf16" and s.variant == "full":
@@ -351,6 +405,12 @@ def main():
     dec = None
     if not args.no_decode and s.dtype == "bf16" and s.variant == "full" and s.T % 32 == 0:
         dec = decode_leg(gq, torch, s, dv, steps, args.warmup, mk_events, args.config)
+
+    others = None
+    if not args.no_configs and s.variant == "full":
+        del dv
+        torch.cuda.empty_cache()
+        others = other_configs(gq, torch, args.config, args.warmup, mk_events)
 
     peak = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
     fl = attn_flops(s, active_heads(s))
@@ -380,6 +440,7 @@ def main():
         "gqa_baseline": gqa,
         "training_step": bwd,
         "decode_step": dec,
+        "configs": others,
         "wall_s_timed_region": wall,
         "cpu_baseline": None,
     }

@@ -249,9 +249,30 @@ gqe_status gqe_attn_fwd_train(const gqe_shape* s, const void* x, const void* Wr,
                               const void* Wo, void* out, int32_t* idx_out, float* w_out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* gqe_attn_fwd_train with the picks given by the caller instead of the
+ * router's: for checking the training pair against a reference routing where
+ * two experts' logits nearly tie, or for routing chosen outside the layer.
+ * The router logits are still computed (the backward's router gradient
+ * needs them) and the weights are the picks' group-softmax probabilities
+ * from those logits, renormalised over the token's G*k picks, exactly as the
+ * router forms them; the backward then differentiates this forward.
+ *   idx    [B*T, G, k] int32   picks, each in [0, M) and distinct within its
+ *                              group; an entry outside [0, M) or repeating an
+ *                              earlier rank's expert is replaced by the
+ *                              group's lowest unused expert (never an
+ *                              out-of-bounds access)
+ *   w_out  [B*T, G, k] fp32    out (NULL to skip): the weights used
+ * Other arguments, errors and the workspace as for gqe_attn_fwd_train;
+ * GQE_ERR_NULL if idx is NULL. */
+gqe_status gqe_attn_fwd_train_routed(const gqe_shape* s, const void* x, const void* Wr, const float* br,
+                                     const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh,
+                                     const void* Wo, const int32_t* idx, void* out, float* w_out,
+                                     void* ws, size_t ws_bytes, void* stream);
+
 /* Backward of the layer. ws must be the workspace of the last
- * gqe_attn_fwd_train with the same shape and inputs on this stream, unchanged
- * since (the call overwrites its backward part).
+ * gqe_attn_fwd_train (or gqe_attn_fwd_train_routed) with the same shape and
+ * inputs on this stream, unchanged since (the call overwrites its backward
+ * part).
  *   x, Wr, Wq, Wk, Wv, Wq_sh, Wo   the forward's inputs (bf16, layouts as in
  *                                  gqe_attn_fwd_routed; br is not needed)
  *   dout     [B*T, D] bf16         gradient of the loss with respect to out

@@ -36,7 +36,7 @@ from . import gqe_oracle as go
 
 __all__ = [
     "attention_backward", "renormalize_backward", "scatter_picks", "group_softmax_backward",
-    "load_balance_loss", "gqe_backward",
+    "load_balance_loss", "gqe_backward", "gqe_backward_rows",
 ]
 
 
@@ -176,3 +176,102 @@ def gqe_backward(inp: dict, fwd: dict, dout: np.ndarray, G: int, M: int, k: int,
     return dict(dx=dx, dWr=dWr, dbr=dbr, dWq=dWq.reshape(G * M * d, D), dWk=dWk, dWv=dWv, dWq_sh=dWq_sh,
                 dWo=dWo, aux_loss=aux, dC=dC, dO=dO, dw=dw, dQr=dQr, dQ_sh=dQ_sh,
                 dK=dKf, dV=dVf, dlogits=dlogits)
+
+
+def gqe_backward_rows(inp: dict, rows, dout_rows: np.ndarray, G: int, M: int, k: int, d: int, B: int, T: int,
+                      shared_kv_group: int = 0) -> dict:
+    """The gradients of gqe_backward when dout is zero on every token except
+    `rows` (dout_rows [len(rows), D] holds theirs) and there is no balancing
+    loss, computed row by row, so that sequences far longer than the full
+    oracle can hold are checked: only the given rows' attention enters
+    (their causal prefixes in full), every key and value of those prefixes
+    receives its dK, dV contribution, and the projections then sum over all
+    tokens. Same formulas as gqe_backward: dV = P^T dO, dS = P * (dP -
+    rowsum(dP * P)), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d); the slots'
+    split dO = dC_hard + w dC_weighted, dw = <O, dC_weighted>; the router
+    through the renormalisation and the group softmax. Returns dx [N,D], dWr,
+    dbr, dWq, dWk, dWv, dWq_sh, dWo and the forward's picks of the rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    x = inp["x"]
+    N, D = x.shape
+    GK = G * k
+    scale = 1.0 / np.sqrt(d)
+    xr = x[rows]
+    logits, p, sel, w = go.route(xr, inp["Wr"], inp.get("br"), G, M, k)
+
+    K = go.project(x, inp["Wk"]).reshape(N, G, d)
+    V = go.project(x, inp["Wv"]).reshape(N, G, d)
+    Wq = inp["Wq"].reshape(G, M, d, D)
+    nR = len(rows)
+    # query of every (row, head): routed heads (g, r), then the shared head
+    q = np.zeros((nR, GK + 1, d))
+    grp = np.empty(GK + 1, dtype=np.int64)
+    for g in range(G):
+        for r in range(k):
+            grp[g * k + r] = g
+            for i in range(nR):
+                q[i, g * k + r] = xr[i] @ Wq[g, sel[i, g, r]].T
+    q[:, GK] = go.project(xr, inp["Wq_sh"])
+    grp[GK] = shared_kv_group
+
+    # forward attention of the rows, kept for the backward
+    P = {}
+    O = np.zeros((nR, GK + 1, d))
+    for i, n in enumerate(rows):
+        b, t = divmod(int(n), T)
+        keys = slice(b * T, b * T + t + 1)
+        for h in range(GK + 1):
+            s_ = (K[keys, grp[h]] @ q[i, h]) * scale
+            e = np.exp(s_ - s_.max())
+            P[i, h] = e / e.sum()
+            O[i, h] = P[i, h] @ V[keys, grp[h]]
+    C = np.concatenate([O[:, :GK].reshape(nR, GK * d), np.einsum("ngr,ngrd->nd", w, O[:, :GK].reshape(nR, G, k, d)),
+                        O[:, GK]], axis=1)
+
+    dWo = dout_rows.T @ C
+    dC = dout_rows @ inp["Wo"]
+    dCw = dC[:, GK * d:(GK + 1) * d]
+    dO = np.zeros((nR, GK + 1, d))
+    dO[:, :GK] = dC[:, :GK * d].reshape(nR, GK, d) + w.reshape(nR, GK)[..., None] * dCw[:, None, :]
+    dO[:, GK] = dC[:, (GK + 1) * d:]
+    dw = np.einsum("nhd,nd->nh", O[:, :GK], dCw).reshape(nR, G, k)
+
+    dK = np.zeros((N, G, d))
+    dV = np.zeros((N, G, d))
+    dq = np.zeros((nR, GK + 1, d))
+    for i, n in enumerate(rows):
+        b, t = divmod(int(n), T)
+        keys = slice(b * T, b * T + t + 1)
+        for h in range(GK + 1):
+            g = grp[h]
+            Ph = P[i, h]
+            dV[keys, g] += np.outer(Ph, dO[i, h])
+            dP = V[keys, g] @ dO[i, h]
+            dS = Ph * (dP - (dP * Ph).sum())
+            dq[i, h] = (dS @ K[keys, g]) * scale
+            dK[keys, g] += np.outer(dS, q[i, h]) * scale
+
+    dx = np.zeros_like(x)
+    dWq = np.zeros_like(Wq)
+    for g in range(G):
+        for r in range(k):
+            for i in range(nR):
+                m = sel[i, g, r]
+                dWq[g, m] += np.outer(dq[i, g * k + r], xr[i])
+                dx[rows[i]] += dq[i, g * k + r] @ Wq[g, m]
+    dWq_sh = dq[:, GK].T @ xr
+    dx[rows] += dq[:, GK] @ inp["Wq_sh"]
+    dKf = dK.reshape(N, G * d)
+    dVf = dV.reshape(N, G * d)
+    dWk = dKf.T @ x
+    dWv = dVf.T @ x
+    dx += dKf @ inp["Wk"] + dVf @ inp["Wv"]
+
+    p_pick = go.pick_probs(p, sel)
+    dp = scatter_picks(renormalize_backward(p_pick, w, dw), sel, M)
+    dlogits = group_softmax_backward(p, dp).reshape(nR, G * M)
+    dWr = dlogits.T @ xr
+    dbr = dlogits.sum(axis=0)
+    dx[rows] += dlogits @ inp["Wr"]
+    return dict(dx=dx, dWr=dWr, dbr=dbr, dWq=dWq.reshape(G * M * d, D), dWk=dWk, dWv=dWv, dWq_sh=dWq_sh,
+                dWo=dWo, idx=sel, rows=rows)

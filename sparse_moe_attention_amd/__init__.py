@@ -14,6 +14,7 @@ Entry points (same names as the C ABI in include/gqe.h):
     gqa_attn_fwd(B, T, D, Hq, G, d_h, dtype, x, Wq, Wk, Wv, Wo, out, ws=None)
     gqe_train_workspace_bytes(shape)
     gqe_attn_fwd_train(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, ws, idx_out=None, w_out=None)
+    gqe_attn_fwd_train_routed(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, idx, out, ws, w_out=None)
     gqe_attn_bwd(shape, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, grads, ws, dbr=None, aux_loss=None)
     gqe_decode_workspace_bytes(shape)
     gqe_decode_step(shape, pos, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, k_cache, vt_cache, out, ws, idx_out=None, w_out=None)
@@ -105,6 +106,8 @@ def load() -> ctypes.CDLL:
     lib.gqe_train_workspace_bytes.argtypes = [SH]
     lib.gqe_train_workspace_bytes.restype = S
     lib.gqe_attn_fwd_train.argtypes = [SH, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gqe_attn_fwd_train_routed.argtypes = [SH, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gqe_attn_fwd_train_routed.restype = ctypes.c_int
     lib.gqe_attn_fwd_train.restype = ctypes.c_int
     bwd = [SH, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gqe_attn_bwd.argtypes = bwd
@@ -259,6 +262,13 @@ def gqe_attn_fwd_train(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, ws, idx_out
     _check(load().gqe_attn_fwd_train(ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(br), _ptr(Wq), _ptr(Wk),
                                      _ptr(Wv), _ptr(Wq_sh), _ptr(Wo), _ptr(out), _ptr(idx_out), _ptr(w_out),
                                      _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def gqe_attn_fwd_train_routed(shape, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, idx, out, ws, w_out=None, stream=None):
+    """gqe_attn_fwd_train with the caller's picks idx [N, G, k] instead of the router's."""
+    _check(load().gqe_attn_fwd_train_routed(ctypes.byref(shape), _ptr(x), _ptr(Wr), _ptr(br), _ptr(Wq), _ptr(Wk),
+                                            _ptr(Wv), _ptr(Wq_sh), _ptr(Wo), _ptr(idx), _ptr(out), _ptr(w_out),
+                                            _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def gqe_attn_bwd(shape, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, grads, ws, dbr=None, aux_loss=None,

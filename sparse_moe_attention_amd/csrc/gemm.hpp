@@ -474,7 +474,11 @@ __device__ __forceinline__ bool skinny_reduce(f32x4& acc, f32x4 (&part)[3][64], 
     return true;
 }
 
+// (A template only so that the kernel is emitted in the one unit that
+// instantiates it, with bf16.)
+template <typename T>
 __global__ __launch_bounds__(256) void skinny_proj_kernel(ProjArgs a) {
+    static_assert(sizeof(T) == 2, "bf16 only");
     __shared__ f32x4 part[3][64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -26,32 +26,12 @@
 #include "attention_bwd.hpp"
 #include "backward.hpp"
 #include "decode.hpp"
-#include "gemm.hpp"
+#include "gemm_launch.hpp"
 #include "route.hpp"
 
 using namespace gqe;
 
 namespace {
-
-// Projection GEMM: 128 x 128 tiles of eight waves (32 x 64 each), two
-// workgroups per CU, four waves per SIMD (T = 32K: K/V projection 107 -> 103
-// us, Wo 83 -> 79 us against four waves of 64 x 64).
-#ifndef GQE_PROJ_CFG
-#define GQE_PROJ_CFG 128, 128, 4, 2, 4
-#endif
-using ProjBf16 = TileCfg<bf16, GQE_PROJ_CFG>;
-using ProjF32 = TileCfg<float, 128, 128, 2, 2>;
-// The grouped routed-Q GEMM: 256 x 64 tiles (256 rows of one expert's
-// segment, its 64 query columns), eight waves of 32 x 64, two workgroups per
-// CU (80 KB of LDS each, 86 VGPRs), so four waves per SIMD. A wave's K step
-// is short (8 MFMAs per 32-wide step), so the tile loads need many waves to
-// hide behind: against 128 x 64 tiles at two per CU, 72 -> 58 us at T = 32K
-// and 367 -> 288 us on the k = 2, D = 2048 workload.
-#ifndef GQE_GRP_CFG
-#define GQE_GRP_CFG 256, 64, 8, 1, 4
-#endif
-using GrpBf16 = TileCfg<bf16, GQE_GRP_CFG>;
-using GrpF32 = TileCfg<float, 128, 64, 4, 1>;
 
 // Sequence padding of the K / V^T buffers: whole key tiles of the forward
 // and whole key blocks of the dK/dV kernel (its waves read their keys' rows).
@@ -146,12 +126,13 @@ template <typename T, class Cfg>
 void launch_proj(ProjArgs& a, int total_cols, hipStream_t st) {
     a.n_tiles_n = (total_cols + Cfg::BN - 1) / Cfg::BN;
     const int64_t n_m = (a.M_rows + Cfg::BM - 1) / Cfg::BM;
-    // Eight resident waves per CU (two per SIMD: the register budget), in
-    // whole XCD rounds.
+    // A persistent grid of the resident workgroups (the register budget's
+    // waves per SIMD), in whole XCD rounds.
     const int64_t tiles = n_m * a.n_tiles_n * (a.n_split > 1 ? a.n_split : 1);
     const int per_cu = std::max(1, Cfg::WPE * 4 / (Cfg::WM * Cfg::WN));
     const int64_t grid = std::min<int64_t>(tiles, per_cu * (int64_t)align_up((size_t)device_cus(), 8));
-    hipLaunchKernelGGL((proj_gemm_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NTH), 0, st, a);
+    if constexpr (sizeof(T) == 2) launch_proj_gemm_bf16(a, (unsigned)grid, st);
+    else launch_proj_gemm_f32(a, (unsigned)grid, st);
 }
 
 struct SegList {
@@ -206,7 +187,7 @@ void run_proj_rows(const Dims& d, SegList& sl, hipStream_t st) {
     }
     sl.a.n_tiles_n = (sl.cols + 15) / 16;
     const int64_t n_m = (sl.a.M_rows + kSkinnyRows - 1) / kSkinnyRows;
-    hipLaunchKernelGGL(skinny_proj_kernel, dim3((unsigned)(n_m * sl.a.n_tiles_n)), dim3(256), 0, st, sl.a);
+    launch_skinny_proj(sl.a, (unsigned)(n_m * sl.a.n_tiles_n), st);
 }
 
 // Routing from the logits (route_kernel<0>): group widths 1, 2, 4, 8 and 16
@@ -238,8 +219,8 @@ void run_grouped_q(const Dims& d, const void* x, const void* Wq, void* Qr, const
     g.n_t = (int)((d.N + bm - 1) / bm);
     // 8 * E * ceil(n_t / 8) workgroups: tile t = 8*(j/E) + hw%8 of expert j%E, j = hw/8.
     const dim3 grid((unsigned)(8 * (int64_t)d.E * ((g.n_t + 7) / 8)));
-    if (d.f32) hipLaunchKernelGGL((grouped_q_kernel<float, GrpF32>), grid, dim3(GrpF32::NTH), 0, st, g);
-    else hipLaunchKernelGGL((grouped_q_kernel<bf16, GrpBf16>), grid, dim3(GrpBf16::NTH), 0, st, g);
+    if (d.f32) launch_grouped_q_f32(g, grid.x, st);
+    else launch_grouped_q_bf16(g, grid.x, st);
 }
 
 // Attention tile shape by sequence length: AttnShort up to T = 256K, AttnLong
@@ -659,16 +640,18 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
     return last_hip();
 }
 
+// idx_in (training only, may be null): the caller's picks replace the router's.
 gqe_status fwd_impl(const gqe_shape* s, const void* x, const void* Wr, const float* br, const void* Wq,
                     const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo, void* out, int32_t* idx_out,
-                    float* w_out, void* ws, size_t ws_bytes, void* stream, void* const* events, bool train) {
+                    float* w_out, void* ws, size_t ws_bytes, void* stream, void* const* events, bool train,
+                    const int32_t* idx_in = nullptr) {
     Dims d;
     gqe_status rc = check_shape(s, &d);
     if (rc != GQE_OK) return rc;
     if (!x || !Wr || !Wq || !Wk || !Wv || !Wq_sh || !Wo || !out || !ws) return GQE_ERR_NULL;
     if (!aligned16(x) || !aligned16(Wr) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
         !aligned16(Wq_sh) || !aligned16(Wo) || !aligned16(out) || !aligned16(ws) || (br && !aligned16(br)) ||
-        (idx_out && !aligned16(idx_out)) || (w_out && !aligned16(w_out)))
+        (idx_out && !aligned16(idx_out)) || (w_out && !aligned16(w_out)) || (idx_in && !aligned16(idx_in)))
         return GQE_ERR_ALIGN;
     if (train && (rc = check_train(d)) != GQE_OK) return rc;
     const GqeWs L = gqe_layout(d);
@@ -689,7 +672,15 @@ gqe_status fwd_impl(const gqe_shape* s, const void* x, const void* Wr, const flo
     sl.add(Wv, d.G * d.d, at(ws, L.Vt), OUT_HEADS_T, 0, nullptr);
     run_proj(d, sl, st);
     mk.at(1);
-    run_route(d, lg, idx, w, (int32_t*)at(ws, L.hist), st);
+    if (idx_in != nullptr) {
+        hipLaunchKernelGGL(inject_route_kernel, dim3((unsigned)((d.N + 255) / 256)), dim3(256), 0, st,
+                           (const float*)lg, idx_in, idx, w, d.N, d.G, d.M, d.k);
+        hipLaunchKernelGGL((route_kernel<1, 0>), dim3((unsigned)d.nC), dim3(kRouteThreads), 0, st,
+                           (const float*)nullptr, idx, (float*)nullptr, (int32_t*)at(ws, L.hist), d.N, d.G, d.M, d.k,
+                           1);
+    } else {
+        run_route(d, lg, idx, w, (int32_t*)at(ws, L.hist), st);
+    }
     rc = run_post_router(d, L, ws, x, Wq, Wk, Wv, Wq_sh, Wo, idx, w, out, at(ws, L.C), st, false, mk,
                          train ? (float*)at(ws, TL.lse) : nullptr, TL.rs.Lr, TL.rs.Lx);
     if (rc != GQE_OK || !train) return rc;
@@ -980,6 +971,15 @@ gqe_status gqe_attn_fwd_train(const gqe_shape* s, const void* x, const void* Wr,
                               const void* Wk, const void* Wv, const void* Wq_sh, const void* Wo, void* out,
                               int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
     return fwd_impl(s, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, idx_out, w_out, ws, ws_bytes, stream, nullptr, true);
+}
+
+gqe_status gqe_attn_fwd_train_routed(const gqe_shape* s, const void* x, const void* Wr, const float* br,
+                                     const void* Wq, const void* Wk, const void* Wv, const void* Wq_sh,
+                                     const void* Wo, const int32_t* idx, void* out, float* w_out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    if (s != nullptr && idx == nullptr) return GQE_ERR_NULL;
+    return fwd_impl(s, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, out, nullptr, w_out, ws, ws_bytes, stream, nullptr, true,
+                    idx);
 }
 
 gqe_status gqe_attn_bwd_timed(const gqe_shape* s, const void* x, const void* Wr, const void* Wq, const void* Wk,

@@ -87,6 +87,43 @@ __device__ inline float renorm_total(int G, int k, Prob&& prob) {
     return total;
 }
 
+// Caller-given picks (the training forward with injected routing): idx_in
+// [N, G, k] is copied to idx, an entry outside [0, M) or repeating an
+// earlier rank's expert in its group replaced by the group's lowest unused
+// expert, so the picks stay a valid set; w gets the picks' group-softmax
+// probabilities from the logits, renormalised over the token's G*k picks, in
+// the router's own arithmetic (topk_group's max and sum, renorm_total's
+// order). One thread per token.
+__global__ __launch_bounds__(256) void inject_route_kernel(const float* __restrict__ logits,
+                                                           const int32_t* __restrict__ idx_in,
+                                                           int32_t* __restrict__ idx, float* __restrict__ w,
+                                                           int64_t N, int G, int M, int k) {
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    const int E = G * M, GK = G * k;
+    const float* z = logits + n * E;
+    const int32_t* src = idx_in + n * GK;
+    int32_t* irow = idx + n * GK;
+    float* wrow = w + n * GK;
+    for (int g = 0; g < G; ++g) {
+        const float* zg = z + g * M;
+        float mx = -INFINITY;
+        for (int m = 0; m < M; ++m) mx = fmaxf(mx, zg[m]);
+        float se = 0.f;
+        for (int m = 0; m < M; ++m) se += expf(zg[m] - mx);
+        uint64_t used = 0;
+        for (int r = 0; r < k; ++r) {
+            int m = src[g * k + r];
+            if (m < 0 || m >= M || ((used >> m) & 1ull)) m = __builtin_ctzll(~used);   // k <= M: one is free
+            used |= 1ull << m;
+            irow[g * k + r] = m;
+            wrow[g * k + r] = expf(zg[m] - mx) / se;
+        }
+    }
+    const float inv = 1.f / renorm_total(G, k, [&](int g, int r) { return wrow[g * k + r]; });
+    for (int j = 0; j < GK; ++j) wrow[j] *= inv;
+}
+
 // MODE 0: route from fp32 logits [N, G*M] -> idx, w and the histogram
 // (renorm = 0: w is the pick's probability, not renormalised). MM as in
 // topk_group. The quarter sums of renorm_total meet in LDS, so w is the same

@@ -220,3 +220,21 @@ def test_noalloc_entry_point_validates(lib):
     # the 32K-token layer and the larger-pool layer fit the scratch
     for sh in (shape(T=32768, D=1024, G=8, M=2, d_h=64), shape(B=2, T=16384, D=2048, G=8, M=4, k=2, d_h=64)):
         assert 0 < lib.gqe_workspace_bytes(ctypes.byref(sh)) <= gq.GQE_NOALLOC_SCRATCH_BYTES
+
+
+def test_train_routed_entry_point_validates(lib):
+    s = shape()
+    need = lib.gqe_train_workspace_bytes(ctypes.byref(s))
+
+    def call(sh, n=need, **o):
+        return lib.gqe_attn_fwd_train_routed(ctypes.byref(sh) if sh is not None else None, A, A, None, A, A, A, A,
+                                             A, o.get("idx", A), o.get("out", A), o.get("w"), A, n, None)
+
+    assert call(None) == -1
+    assert call(s, idx=None) == -1
+    assert call(s, out=None) == -1
+    assert call(s, idx=BAD) == -5
+    assert call(s, w=BAD) == -5
+    assert call(s, n=need - 1) == -4
+    assert call(shape(k=3)) == -2
+    assert call(shape(dtype=gq.GQE_F32), n=1 << 40) == -3

@@ -150,8 +150,46 @@ def pin_load_balance_loss_count():
     assert math.isclose(loss, 1.0, rel_tol=1e-12)
 
 
+def pin_rows_backward_against_full():
+    """The row-by-row backward (dout zero outside a few rows, no balancing
+    loss) against the full-matrix backward on the same inputs: two shapes,
+    one with k = 2, a biased router, two sequences and the shared head on
+    group 1; rows at both sequences' ends, their starts and the middle. Then
+    finite differences of the forward oracle along random directions, with
+    dout zero outside the rows."""
+    for seed, (B, T, D, G, M, k, d, s0) in ((41, (2, 37, 24, 3, 3, 2, 8, 1)), (43, (1, 70, 16, 2, 2, 1, 8, 0))):
+        rng = np.random.default_rng(seed)
+        inp = rand_layer(rng, B, T, D, G, M, k, d, bias=True)
+        inp.pop("Wo_gqa")
+        N = B * T
+        rows = np.array(sorted({0, T - 1, N - 1, N - 3, T // 2, N - T}))
+        dout = np.zeros((N, D))
+        dout[rows] = rng.standard_normal((len(rows), D))
+        fwd = go.gqe_forward(inp, G, M, k, d, B, T, shared_kv_group=s0, q_block=16)
+        full = gb.gqe_backward(inp, fwd, dout, G, M, k, d, B, T, shared_kv_group=s0, aux_coef=0.0, q_block=16)
+        part = gb.gqe_backward_rows(inp, rows, dout[rows], G, M, k, d, B, T, shared_kv_group=s0)
+        assert (part["idx"] == fwd["idx"][rows]).all()
+        for name in PARAMS:
+            a, b = part[GRAD[name]], full[GRAD[name]]
+            assert np.allclose(a, b, rtol=1e-9, atol=1e-12 * max(1.0, np.abs(b).max())), name
+        h = 1e-5
+        for name in PARAMS:
+            v = rng.standard_normal(inp[name].shape)
+            Ls = []
+            for sgn in (1.0, -1.0):
+                pert = dict(inp)
+                pert[name] = inp[name] + sgn * h * v
+                f = go.gqe_forward(pert, G, M, k, d, B, T, shared_kv_group=s0, q_block=16)
+                assert np.array_equal(f["idx"], fwd["idx"])
+                Ls.append(float((dout * f["out"]).sum()))
+            fd = (Ls[0] - Ls[1]) / (2 * h)
+            an = float((part[GRAD[name]] * v).sum())
+            assert abs(fd - an) <= 2e-7 * max(1.0, abs(fd)), (name, fd, an)
+
+
 PINS = [pin_layer_finite_differences, pin_attention_torch_autograd, pin_softmax_torch_autograd,
-        pin_gradient_invariants, pin_router_learns_only_through_weighted_slot, pin_load_balance_loss_count]
+        pin_gradient_invariants, pin_router_learns_only_through_weighted_slot, pin_load_balance_loss_count,
+        pin_rows_backward_against_full]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
