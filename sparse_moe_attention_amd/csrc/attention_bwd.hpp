@@ -152,10 +152,13 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
-    // Workgroup -> (level = key tile, unit = group x sequence); units of one
-    // level run back to back, longest (earliest keys) first.
+    // Workgroup -> (level = key tile, unit = group x sequence); levels run
+    // longest (earliest keys) first. Workgroup i runs on XCD i % 8, so with a
+    // fixed unit order each group would stay on one XCD and the XCD of a group
+    // with more rows per token (the shared head's) would take the longest;
+    // rotating the units by one per level spreads every group over all XCDs.
     const int units = a.G * a.rs.Bt;
-    const int kt = blockIdx.x / units, unit = blockIdx.x % units;
+    const int kt = blockIdx.x / units, unit = (blockIdx.x % units + kt) % units;
     const int g = unit / a.rs.Bt, b = unit % a.rs.Bt;
     const int64_t T_ = a.rs.T;
     const int k0 = kt * kBwdBK;
@@ -408,9 +411,11 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
     // Workgroup -> (level, unit); level l takes row tile n_t(g) - 1 - l, so
-    // the longest tiles of every group and sequence come first.
+    // the longest tiles of every group and sequence come first. The units
+    // rotate by one per level, which spreads every group (the shared head's
+    // has more row tiles) over all XCDs.
     const int units = a.G * a.rs.Bt;
-    const int lv = blockIdx.x / units, unit = blockIdx.x % units;
+    const int lv = blockIdx.x / units, unit = (blockIdx.x % units + lv) % units;
     const int g = unit / a.rs.Bt, b = unit % a.rs.Bt;
     const int Rg = rs_R(a.rs, g);
     const int64_t T_ = a.rs.T;
