@@ -152,15 +152,12 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
-    // Workgroup -> (level = key tile, unit = group x sequence); levels run
-    // longest (earliest keys) first. Workgroup i runs on XCD i % 8, so with a
-    // fixed unit order each group would stay on one XCD and the XCD of a group
-    // with more rows per token (the shared head's) would take the longest;
-    // rotating the units by one per level spreads every group over all XCDs.
-    const int units = a.G * a.rs.Bt;
-    const int kt = blockIdx.x / units, unit = (blockIdx.x % units + kt) % units;
-    const int g = unit / a.rs.Bt, b = unit % a.rs.Bt;
+    // Workgroup -> (group, sequence, key tile), longest jobs first over both
+    // row classes (bwd_job).
     const int64_t T_ = a.rs.T;
+    const int64_t n_k = (T_ + kBwdBK - 1) / kBwdBK;
+    const BwdJob job = bwd_job(blockIdx.x, a.rs, a.G, n_k, DkdvSplit{T_, kBwdBK, n_k, a.rs.R});
+    const int g = job.g, b = job.b, kt = (int)job.j;
     const int k0 = kt * kBwdBK;
     if (k0 >= T_) return;
     const int Rg = rs_R(a.rs, g);
@@ -410,18 +407,16 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
-    // Workgroup -> (level, unit); level l takes row tile n_t(g) - 1 - l, so
-    // the longest tiles of every group and sequence come first. The units
-    // rotate by one per level, which spreads every group (the shared head's
-    // has more row tiles) over all XCDs.
-    const int units = a.G * a.rs.Bt;
-    const int lv = blockIdx.x / units, unit = (blockIdx.x % units + lv) % units;
-    const int g = unit / a.rs.Bt, b = unit % a.rs.Bt;
-    const int Rg = rs_R(a.rs, g);
+    // Workgroup -> (group, sequence, row tile counted from the last), longest
+    // jobs first over both row classes (bwd_job).
     const int64_t T_ = a.rs.T;
+    const int64_t n_r = (T_ * a.rs.R + BQ - 1) / BQ, n_x = (T_ * (a.rs.R + 1) + BQ - 1) / BQ;
+    const BwdJob job = bwd_job(blockIdx.x, a.rs, a.G, n_r, DqSplit{n_r, n_x});
+    const int g = job.g, b = job.b;
+    const int Rg = rs_R(a.rs, g);
     const int64_t Lreal = T_ * Rg;
     const int n_t = (int)((Lreal + BQ - 1) / BQ);
-    const int qt = n_t - 1 - lv;
+    const int qt = n_t - 1 - (int)job.j;
     if (qt < 0) return;
     const int64_t base = rs_base(a.rs, g, b);
     const int64_t row0 = (int64_t)qt * BQ + wave * QW;    // first row of this wave

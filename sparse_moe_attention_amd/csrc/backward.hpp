@@ -37,6 +37,82 @@ __host__ __device__ inline int64_t rs_base(const RowSpace& s, int g, int b) {
 }
 
 // ---------------------------------------------------------------------------
+// Order of the attention-backward workgroups. Each (group, sequence) stream
+// has a run of jobs of decreasing work; the regular streams (nrb of them) all
+// have n_r jobs and the same work at the same index, the shared head's group
+// (xb streams, one per sequence) has n_x jobs. Workgroups are issued in
+// order of decreasing work across both classes: "level" l holds the extra
+// jobs [P(l), P(l+1)) of every extra stream, then job l of every regular
+// stream; a last level n_r holds the remaining extra jobs. P is the caller's
+// split (P(0) = 0, P(n_r + 1) = n_x, non-decreasing). Workgroup i runs on
+// XCD i % 8, so this order hands every XCD the same mix of long and short
+// jobs; a fixed stream-to-XCD map would leave the XCD of the heavier class
+// with about twice the work of the others.
+// ---------------------------------------------------------------------------
+struct BwdJob {
+    int g, b;     // group and sequence
+    int64_t j;    // job index within the stream (0 = the longest)
+};
+template <class Split>
+__host__ __device__ inline int64_t bwd_job_count(int64_t l, int64_t nrb, int64_t xb, int64_t n_r, Split P) {
+    return xb * P(l) + nrb * (l < n_r ? l : n_r);
+}
+template <class Split>
+__host__ __device__ inline BwdJob bwd_job(int64_t L, const RowSpace& rs, int G, int64_t n_r, Split P) {
+    const bool xc = rs.s0 >= 0;
+    const int64_t xb = xc ? rs.Bt : 0, nrb = (int64_t)rs.Bt * (xc ? G - 1 : G);
+    int64_t lo = 0, hi = n_r + 1;            // count(lo) <= L < count(hi)
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) / 2;
+        if (bwd_job_count(mid, nrb, xb, n_r, P) <= L) lo = mid;
+        else hi = mid;
+    }
+    const int64_t p = L - bwd_job_count(lo, nrb, xb, n_r, P);
+    const int64_t nxl = xb * (P(lo + 1) - P(lo));
+    BwdJob r;
+    if (p < nxl) {
+        r.g = rs.s0;
+        r.b = (int)(p % rs.Bt);
+        r.j = P(lo) + p / rs.Bt;
+    } else {
+        const int64_t u = p - nxl;
+        const int gi = (int)(u / rs.Bt);
+        r.g = (xc && gi >= rs.s0) ? gi + 1 : gi;
+        r.b = (int)(u % rs.Bt);
+        r.j = lo;
+    }
+    return r;
+}
+// Total jobs of both classes.
+__host__ __device__ inline int64_t bwd_jobs(const RowSpace& rs, int G, int64_t n_r, int64_t n_x) {
+    return (int64_t)rs.Bt * (rs.s0 >= 0 ? (int64_t)(G - 1) * n_r + n_x : (int64_t)G * n_r);
+}
+// dK/dV: job j of a stream is key tile j (BK keys), whose work is the rows
+// from its first key on: (T - j*BK) * Rg. Extra job j goes before regular
+// level l when its work is at least that of level l - 1.
+struct DkdvSplit {
+    int64_t T, BK, n;
+    int R;
+    __host__ __device__ int64_t operator()(int64_t l) const {
+        if (l <= 0) return 0;
+        if (l > n) return n;
+        const int64_t f = (T + (l - 1) * BK * R) / (BK * (R + 1)) + 1;   // extra jobs at least as long as level l - 1
+        return f < n ? f : n;
+    }
+};
+// dQ: job j of a stream is its row tile counted from the last; regular and
+// extra tiles that end at about the same token are about as long, so the
+// extra jobs are spread in proportion, P(l) = l * n_x / n_r.
+struct DqSplit {
+    int64_t n_r, n_x;
+    __host__ __device__ int64_t operator()(int64_t l) const {
+        if (l <= 0) return 0;
+        if (l > n_r) return n_x;
+        return l * n_x / n_r;
+    }
+};
+
+// ---------------------------------------------------------------------------
 // dst[x][y] = src[y][x] for y < R, x < C; 0 elsewhere in the dst box
 // [Co rows x Ro cols]. One 64x64 tile per workgroup through LDS: blockIdx.x
 // = tile (ty + nty * tx), blockIdx.y steps src by zs and dst by zd elements.

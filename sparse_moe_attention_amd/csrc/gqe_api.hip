@@ -603,7 +603,7 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
     {
         const int bk = d.d == 64 ? bwd_bk<64>() : bwd_bk<32>();
         ab.n_tiles = (int)((d.T + bk - 1) / bk);
-        const dim3 grid((unsigned)((int64_t)ab.n_tiles * d.G * d.B));
+        const dim3 grid((unsigned)bwd_jobs(L.rs, (int)d.G, ab.n_tiles, ab.n_tiles));
         if (d.d == 64) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, dim3(bwd_nw<64>() * 64), 0, st, ab);
         else hipLaunchKernelGGL(attn_bwd_dkdv_kernel<32>, grid, dim3(bwd_nw<32>() * 64), 0, st, ab);
     }
@@ -613,7 +613,7 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
         const bool lng = d.d == 64 && d.T > kAttnLongT;
         const int bq = lng ? DqLong::BQ : DqShort::BQ;
         ab.n_tiles = (int)((d.T * (d.k + 1) + bq - 1) / bq);
-        const dim3 grid((unsigned)((int64_t)ab.n_tiles * d.G * d.B));
+        const dim3 grid((unsigned)bwd_jobs(L.rs, (int)d.G, (d.T * d.k + bq - 1) / bq, ab.n_tiles));
         if (lng) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, DqLong>), grid, dim3(DqLong::NW * 64), 0, st, ab);
         else if (d.d == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<64, DqShort>), grid, dim3(DqShort::NW * 64), 0, st, ab);
         else hipLaunchKernelGGL((attn_bwd_dq_kernel<32, DqShort>), grid, dim3(DqShort::NW * 64), 0, st, ab);
