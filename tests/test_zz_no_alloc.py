@@ -70,3 +70,44 @@ def test_noalloc_rejects_shapes_beyond_the_scratch():
     with pytest.raises(gq.GqeError) as e:
         gq.gqe_attn_fwd_noalloc(gq.shape_from(s), x, x, None, x, x, x, x, x, x)
     assert e.value.code == -7
+
+
+def test_noalloc_graph_replays_match_eager():
+    """The entry point's callers include HIP-graph capture: capture one
+    gqe_attn_fwd_noalloc call, replay it three times with an eager call on
+    another shape in between (which overwrites the shared scratch), and check
+    every replay bit for bit against the workspace form."""
+    s, seed = CASES[1][1], 5
+    other, oseed = CASES[2][1], 6
+    dv = H.to_device(make_inputs(s, seed=seed))
+    dvo = H.to_device(make_inputs(other, seed=oseed))
+    ref = H.alloc_outputs(s)
+    H.run_gqe(s, dv, ref)
+    got = H.alloc_outputs(s)
+    oth = H.alloc_outputs(other)
+
+    def call():
+        gq.gqe_attn_fwd_noalloc(gq.shape_from(s), dv["x"], dv["Wr"], dv["br"], dv["Wq"], dv["Wk"], dv["Wv"],
+                                dv["Wq_sh"], dv["Wo"], got["out"], got["idx"], got["w"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                       # first call on the device sets the scratch up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        for t in got.values():
+            t.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in ("out", "idx", "w"):
+            assert torch.equal(got[key], ref[key]), (r, key)
+        gq.gqe_attn_fwd_noalloc(gq.shape_from(other), dvo["x"], dvo["Wr"], dvo["br"], dvo["Wq"], dvo["Wk"],
+                                dvo["Wv"], dvo["Wq_sh"], dvo["Wo"], oth["out"], oth["idx"], oth["w"])
+        torch.cuda.synchronize()
+        print(f"[noalloc graph] replay {r} bit-identical to the workspace form", flush=True)
