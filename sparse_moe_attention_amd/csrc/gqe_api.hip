@@ -716,10 +716,11 @@ struct DecodeWs {
 DecodeWs decode_layout(const Dims& c, const Dims& t) {
     DecodeWs L;
     L.tok = gqe_layout(t);
-    // The largest of 512, 256 and 128 keys per wave that still launches 512
-    // workgroups (two per CU): a short cache takes shorter chunks.
+    // The largest of 512, 256, 128 and 64 keys per wave that still launches
+    // 1024 workgroups (four per CU): a short cache takes shorter chunks (at
+    // 2K positions 64 keys per wave: 13.5 us against 15.1 with 128).
     L.cw = 512;
-    while (L.cw > 128 && (int64_t)c.B * c.G * ((c.T + kDecNW * L.cw - 1) / (kDecNW * L.cw)) < 512) L.cw /= 2;
+    while (L.cw > 64 && (int64_t)c.B * c.G * ((c.T + kDecNW * L.cw - 1) / (kDecNW * L.cw)) < 1024) L.cw /= 2;
     L.n_ch = (int)((c.T + kDecNW * L.cw - 1) / (kDecNW * L.cw));
     L.R16 = (int)align_up((size_t)(c.k + 1), 16);
     size_t o = L.tok.total;
@@ -817,11 +818,13 @@ gqe_status decode_impl(const gqe_shape* s, const int32_t* pos, const void* x, co
     if (c.d == 64) {
         if (L.cw == 512) hipLaunchKernelGGL((attn_decode_kernel<64, 512>), grid, blk, 0, st, a);
         else if (L.cw == 256) hipLaunchKernelGGL((attn_decode_kernel<64, 256>), grid, blk, 0, st, a);
-        else hipLaunchKernelGGL((attn_decode_kernel<64, 128>), grid, blk, 0, st, a);
+        else if (L.cw == 128) hipLaunchKernelGGL((attn_decode_kernel<64, 128>), grid, blk, 0, st, a);
+        else hipLaunchKernelGGL((attn_decode_kernel<64, 64>), grid, blk, 0, st, a);
     } else {
         if (L.cw == 512) hipLaunchKernelGGL((attn_decode_kernel<32, 512>), grid, blk, 0, st, a);
         else if (L.cw == 256) hipLaunchKernelGGL((attn_decode_kernel<32, 256>), grid, blk, 0, st, a);
-        else hipLaunchKernelGGL((attn_decode_kernel<32, 128>), grid, blk, 0, st, a);
+        else if (L.cw == 128) hipLaunchKernelGGL((attn_decode_kernel<32, 128>), grid, blk, 0, st, a);
+        else hipLaunchKernelGGL((attn_decode_kernel<32, 64>), grid, blk, 0, st, a);
     }
     mk.at(2);
     bf16* C = (bf16*)at(ws, F.C);
