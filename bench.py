@@ -11,8 +11,10 @@ MFMA roofline fraction (timed live with HIP events on the library's stream),
 the speedup over dense 16q/8kv GQA built from the same kernels, the training
 step (forward that keeps its state + backward, with the attention backward's
 MFMA rate), a decode step (16 sequences over a dense KV cache of the
-workload's length, with the cache read's HBM rate), and the fp64 oracle timed
-on the host's cores (a baseline only).
+workload's length, with the cache read's HBM rate), the chip's sustained
+matrix-core rate from a register-only MFMA load (the published peak assumes a
+clock the power limit does not hold), and the fp64 oracle timed on the host's
+cores (a baseline only).
 """
 from __future__ import annotations
 
@@ -274,6 +276,32 @@ def decode_leg(gq, torch, s, dv, steps, warmup, mk_events, cid):
                               "algorithmic_bytes_per_launch": kv_bytes, "avg_launch_ms": attn_ms}}
 
 
+def mfma_probe_leg(gq, torch, mk_events, launches: int = 5):
+    """The sustained bf16 matrix-core rate of this chip: gqe_mfma_probe keeps
+    every SIMD issuing 16x16x32 bf16 products from registers (no memory
+    traffic) for several milliseconds per launch, long enough to reach the
+    clock the power limit holds. The implied clock assumes one product per
+    SIMD every 16 cycles (1024 flops per SIMD per cycle, 1024 SIMDs)."""
+    wgs, iters = 256 * 8, 8000
+    out = torch.empty(wgs, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        gq.gqe_mfma_probe(wgs, iters, out)
+    e0, e1 = mk_events(2)
+    e0.record(stream)
+    for _ in range(launches):
+        gq.gqe_mfma_probe(wgs, iters, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("gqe_mfma_probe: non-finite checksum")
+    fl = wgs * 4 * iters * 8 * 16384.0
+    tf = fl / (ms / 1e3) / 1e12
+    return {"kernel": "mfma_probe_kernel", "tflops": tf, "frac_of_published": tf / PEAK_BF16_TFLOPS,
+            "implied_clock_ghz": tf * 1e12 / (1024 * 1024) / 1e9, "avg_launch_ms": ms}
+
+
 def source_sha(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -412,9 +440,12 @@ def main():
         torch.cuda.empty_cache()
         others = other_configs(gq, torch, args.config, args.warmup, mk_events)
 
+    probe = mfma_probe_leg(gq, torch, mk_events)
     peak = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
     fl = attn_flops(s, active_heads(s))
     achieved = fl / (attn_ms / 1e3) / 1e12
+    if s.dtype == "bf16":
+        probe["attn_frac_of_sustained"] = achieved / probe["tflops"]
     traffic = measured_traffic(f"config{args.config}", ATTN_SRC)
     rec = {
         "metric": METRIC,
@@ -436,6 +467,7 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
                      "algorithmic_flops_per_launch": fl, "avg_launch_ms": attn_ms},
         "layer_mfma_frac": layer_flops(s) / (ms_step / 1e3) / 1e12 / peak,
+        "mfma_sustained": probe,
         "stage_ms": stage_ms,
         "gqa_baseline": gqa,
         "training_step": bwd,

@@ -344,6 +344,19 @@ gqe_status gqe_decode_step_timed(const gqe_shape* s, const int32_t* pos, const v
                                  void* out, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
                                  void* stream, void* const* events);
 
+/* Diagnostic, not an operation of the pages: the device's sustained bf16
+ * matrix-core rate, to put the kernels' rates in context (the published
+ * dense peak assumes 2.4 GHz; under a sustained matrix load the chip is
+ * power-limited). Launches `workgroups` workgroups of four waves; each wave
+ * issues `iters` rounds of eight independent v_mfma_f32_16x16x32_bf16 on
+ * register operands (no memory traffic in the loop), i.e.
+ * workgroups * 4 * iters * 8 * 16384 flops, and writes one float per
+ * workgroup to out (device, [workgroups], a checksum that keeps the work
+ * live). Time it with events on `stream`.
+ * Errors: GQE_ERR_NULL (out), GQE_ERR_SHAPE (workgroups < 1 or > 2^20,
+ * iters < 1), GQE_ERR_ALIGN (out not 16-byte aligned), GQE_ERR_HIP. */
+gqe_status gqe_mfma_probe(int64_t workgroups, int32_t iters, float* out, void* stream);
+
 /* A static, NUL-terminated description of a status code. */
 const char* gqe_status_str(gqe_status st);
 

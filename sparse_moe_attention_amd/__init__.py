@@ -18,6 +18,7 @@ Entry points (same names as the C ABI in include/gqe.h):
     gqe_attn_bwd(shape, x, Wr, Wq, Wk, Wv, Wq_sh, Wo, dout, aux_coef, grads, ws, dbr=None, aux_loss=None)
     gqe_decode_workspace_bytes(shape)
     gqe_decode_step(shape, pos, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, k_cache, vt_cache, out, ws, idx_out=None, w_out=None)
+    gqe_mfma_probe(workgroups, iters, out)
     gqe_status_str(code)
 """
 from __future__ import annotations
@@ -121,6 +122,8 @@ def load() -> ctypes.CDLL:
     lib.gqe_decode_step.restype = ctypes.c_int
     lib.gqe_decode_step_timed.argtypes = dec + [P]
     lib.gqe_decode_step_timed.restype = ctypes.c_int
+    lib.gqe_mfma_probe.argtypes = [I64, I32, P, P]
+    lib.gqe_mfma_probe.restype = ctypes.c_int
     lib.gqe_status_str.argtypes = [ctypes.c_int]
     lib.gqe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -305,3 +308,10 @@ def gqe_decode_step(shape, pos, x, Wr, br, Wq, Wk, Wv, Wq_sh, Wo, k_cache, vt_ca
         _check(lib.gqe_decode_step(*args))
     else:
         _check(lib.gqe_decode_step_timed(*args, events))
+
+
+def gqe_mfma_probe(workgroups, iters, out, stream=None):
+    """Diagnostic matrix-core load: workgroups * 4 waves * iters * 8 bf16
+    16x16x32 products (16384 flops each), no memory traffic; out: float32
+    device tensor of `workgroups` entries (a checksum)."""
+    _check(load().gqe_mfma_probe(int(workgroups), int(iters), _ptr(out), _stream(stream)))

@@ -875,6 +875,36 @@ gqe_status scratch_base(void** out) {
 
 }  // namespace
 
+// Sustained matrix-core rate: each wave keeps eight independent accumulator
+// chains of v_mfma_f32_16x16x32_bf16 on fixed register operands (distinct,
+// non-trivial bf16 values per lane), so the loop is matrix work only. Two
+// or more waves per SIMD keep the accumulators in ordinary VGPRs (a
+// one-wave budget would put them in AGPRs, which the compiler then shuffles).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) void mfma_probe_kernel(int iters, float* out) {
+    const int lane = threadIdx.x & 63;
+    Frag<bf16> a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a.v[i] = (bf16)(0.25f + 0.01f * (float)((lane * 7 + i * 3) % 29));
+        b.v[i] = (bf16)(0.5f - 0.013f * (float)((lane * 5 + i * 11) % 31));
+    }
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, (float)j};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = mma16(a, b, acc[j]);
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    __shared__ float red[4];
+    // lane 0 of each wave: its lane's share (enough to keep the work live)
+    if (lane == 0) red[threadIdx.x >> 6] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
 extern "C" {
 
 size_t gqe_workspace_bytes(const gqe_shape* s) {
@@ -1108,6 +1138,14 @@ gqe_status gqa_attn_fwd(int64_t B, int64_t T, int64_t D, int32_t Hq, int32_t G, 
                         const void* x, const void* Wq, const void* Wk, const void* Wv, const void* Wo, void* out,
                         void* ws, size_t ws_bytes, void* stream) {
     return gqa_attn_fwd_timed(B, T, D, Hq, G, d_h, dtype, x, Wq, Wk, Wv, Wo, out, ws, ws_bytes, stream, nullptr);
+}
+
+gqe_status gqe_mfma_probe(int64_t workgroups, int32_t iters, float* out, void* stream) {
+    if (out == nullptr) return GQE_ERR_NULL;
+    if (workgroups < 1 || workgroups > (int64_t)1 << 20 || iters < 1) return GQE_ERR_SHAPE;
+    if (!aligned16(out)) return GQE_ERR_ALIGN;
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream, iters, out);
+    return last_hip();
 }
 
 const char* gqe_status_str(gqe_status st) {

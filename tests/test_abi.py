@@ -238,3 +238,13 @@ def test_train_routed_entry_point_validates(lib):
     assert call(s, n=need - 1) == -4
     assert call(shape(k=3)) == -2
     assert call(shape(dtype=gq.GQE_F32), n=1 << 40) == -3
+
+
+def test_mfma_probe_validates(lib):
+    """gqe_mfma_probe rejects a null or misaligned output and out-of-range
+    sizes before it launches anything."""
+    assert lib.gqe_mfma_probe(1024, 10, None, None) == -1
+    assert lib.gqe_mfma_probe(0, 10, A, None) == -2
+    assert lib.gqe_mfma_probe((1 << 20) + 1, 10, A, None) == -2
+    assert lib.gqe_mfma_probe(1024, 0, A, None) == -2
+    assert lib.gqe_mfma_probe(1024, 10, BAD, None) == -5

@@ -109,3 +109,24 @@ def test_segments_and_determinism():
     assert c.sum() == s.N * s.G * s.k
     # the biased router really skews the loads
     assert c.max() > 2 * c.min()
+
+
+def test_mfma_probe_rate_is_plausible():
+    """The matrix-core probe runs, its checksum is finite and identical over
+    two launches, and the rate it implies stays below the published dense
+    bf16 peak (2.5 PFLOP/s at 2.4 GHz) and above a third of it."""
+    wgs, iters = 2048, 2000
+    out = torch.empty(wgs, dtype=torch.float32, device="cuda")
+    gq.gqe_mfma_probe(wgs, iters, out)
+    torch.cuda.synchronize()
+    first = out.clone()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gq.gqe_mfma_probe(wgs, iters, out)
+    e1.record()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    assert torch.equal(out, first)
+    tflops = wgs * 4 * iters * 8 * 16384.0 / (e0.elapsed_time(e1) / 1e3) / 1e12
+    print(f"mfma probe: {tflops:.0f} TFLOP/s", flush=True)
+    assert 2500.0 / 3 < tflops < 2500.0 * 1.02
