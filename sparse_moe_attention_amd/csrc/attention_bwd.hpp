@@ -18,13 +18,17 @@
 //     d = 64, 128 at d = 32);
 //     each wave keeps 32 keys' K and V as resident MFMA operands and
 //     accumulates their dK^T, dV^T over every query row at or after the
-//     keys, 64 rows per step staged in LDS (Q, dO row-major for the score
-//     products, Q^T and dO^T for the accumulations, lse and delta);
+//     keys, 64 rows per step staged in LDS (Q and dO row-major, lse and
+//     delta);
 //   * attn_bwd_dq_kernel: one workgroup per (group, sequence, 128 rows: four
 //     waves of 32), three per CU as in the forward; each wave keeps its 32
 //     rows' Q and dO resident and
-//     walks the key tiles up to its last token, staging K, V (row-major) and
-//     K^T in LDS, accumulating dQ^T = K^T dS^T.
+//     walks the key tiles up to its last token, staging K and V (row-major)
+//     in LDS, accumulating dQ^T = K^T dS^T.
+// The accumulations contract over rows (dK/dV) or keys (dQ), so their
+// operands Q^T, dO^T and K^T are read from the same row-major LDS tiles with
+// gfx950's transposing LDS read (ld_frag_tr): no transposed copies are made
+// or staged.
 // Score blocks are oriented so that the probabilities / score gradients a
 // lane holds after the exponent are exactly the fragment the next product
 // wants (no shuffles): the rows of a 16-row block are permuted so that the 8
@@ -41,14 +45,11 @@ namespace gqe {
 
 struct AttnBwdArgs {
     const bf16* Q;        // [rows][d], row space of RowSpace (pre-scaled queries)
-    const bf16* Qt;       // per sequence [d][L]
     const bf16* dO;       // [rows][d]
-    const bf16* dOt;      // per sequence [d][L]
     const float* lse;     // [rows] -lse, -inf on padding rows
     const float* dlt;     // [rows] -delta
-    const bf16* K;        // [G][Bt][Tpad][d]
+    const bf16* K;        // [G][Bt][Tpad][d], zero beyond T
     const bf16* V;        // [G][Bt][Tpad][d], zero beyond T
-    const bf16* Kt;       // [G][d][Bt*Tpad], zero beyond T
     bf16* dY;             // [N][ldy] gradient matrix
     const int32_t* idx;   // [N][G*k]
     int64_t ldy;
@@ -63,7 +64,7 @@ struct AttnBwdArgs {
 // sub-step, waves per SIMD the registers are sized for; the dQ kernel: rows
 // per wave, waves, keys per sub-step, waves per SIMD, keys per staged tile).
 // The dQ kernel runs three four-wave workgroups per CU (64-key tiles keep
-// their LDS at 48 KB, 32-key sub-steps their registers at 168): the waves
+// their LDS at 32 KB, 32-key sub-steps their registers at 168): the waves
 // sharing a SIMD then come from independent workgroups and overlap one
 // another's exponent and product phases (10% faster than one eight-wave
 // workgroup of 128-key tiles per CU at T = 32K). The dK/dV kernel at d = 64
@@ -127,6 +128,29 @@ static_assert(kBwdKW % 16 == 0 && kBwdQB % kBwdRS == 0 && kBwdRS % 32 == 0, "dK/
 // 32j + 8*(lane/16) .. +7.
 __device__ __forceinline__ int qrow_of(int qb, int i) { return key_of_row(qb, i); }
 
+// A operand of a product that contracts over 32 consecutive rows of a
+// row-major bf16 LDS tile (rows r0 .. r0+31 of columns c0 .. c0+15, 16-byte
+// chunks placed by k_chunk_off<CH>): lane (q4 = lane/16, i = lane%16) gets
+// column c0 + i of rows r0 + 8*q4 .. +7, the layout that reading the
+// transposed tile with one 16-byte load would give. gfx950's transposing
+// read (ds_read_b64_tr_b16) hands lane i of each 16-lane group element i%4
+// of the 8-byte reads of lanes 4e + i/4, e = 0..3 (lane layout checked on
+// the device), so lane i reads 4 columns c0 + 4*(i%4) .. +3 of row
+// r0 + 8*q4 + i/4, and once more 4 rows further for elements 4..7.
+template <int CH>
+__device__ __forceinline__ Frag<bf16> ld_frag_tr(const char* tile, int r0, int c0, int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int q4 = lane >> 4, i = lane & 15;
+    const int r = r0 + 8 * q4 + (i >> 2), c = c0 + 4 * (i & 3);
+    const char* p0 = tile + k_chunk_off<CH>(r, c >> 3) + (c & 7) * 2;
+    const char* p1 = tile + k_chunk_off<CH>(r + 4, c >> 3) + (c & 7) * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+    Frag<bf16> f;
+    f.v = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+}
+
 template <int D>
 __global__ __launch_bounds__(bwd_nw<D>() * 64) __attribute__((amdgpu_waves_per_eu(GQE_BWD_WPE, GQE_BWD_WPE)))
 void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
@@ -136,16 +160,13 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     constexpr int DK = D / 32;                 // contraction steps over d
     constexpr int CB = D / 16;                 // 16-row blocks of dK^T / dV^T
     constexpr int QCH = D / 8;                 // 16-byte chunks per Q / dO row
-    constexpr int TCH = kBwdQB / 8;            // 16-byte chunks per Q^T / dO^T row (64 rows)
     constexpr int QBS = kBwdRS / 16;           // 16-row blocks per sub-step
     constexpr int NSUB = kBwdQB / kBwdRS;
     constexpr int R_BYTES = kBwdQB * D * 2;    // one row-major tile
-    constexpr int T_BYTES = D * kBwdQB * 2;    // one transposed tile
     constexpr int AUX = 1024;                  // lse (256 B), delta (256 B), padding
-    constexpr int STAGE = 2 * R_BYTES + 2 * T_BYTES + AUX;
+    constexpr int STAGE = 2 * R_BYTES + AUX;
     constexpr int R_PER_T = kBwdQB * QCH / NT;
-    constexpr int T_PER_T = D * TCH / NT;
-    static_assert(kBwdQB * QCH % NT == 0 && D * TCH % NT == 0, "tiles split evenly over the threads");
+    static_assert(kBwdQB * QCH % NT == 0, "tiles split evenly over the threads");
     __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
     __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
@@ -161,7 +182,7 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     const int k0 = kt * kBwdBK;
     if (k0 >= T_) return;
     const int Rg = rs_R(a.rs, g);
-    const int64_t L = rs_L(a.rs, g), Lreal = T_ * Rg;
+    const int64_t Lreal = T_ * Rg;
     const int64_t base = rs_base(a.rs, g, b);
     const int kw = k0 + wave * kBwdKW;                    // first key of this wave
 
@@ -191,21 +212,13 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 
     // Direct global->LDS staging; per-thread offsets relative to the step's first row.
     int roff[R_PER_T];
-    int toff[T_PER_T];
 #pragma unroll
     for (int i = 0; i < R_PER_T; ++i) {
         const int s = tid + NT * i, r = s / QCH, p = s % QCH;
         roff[i] = r * D + (p ^ (((r & 3) | (((r >> 3) & 1) << 2)) & (QCH - 1))) * 8;
     }
-#pragma unroll
-    for (int i = 0; i < T_PER_T; ++i) {
-        const int s = tid + NT * i, r = s / TCH, p = s % TCH;
-        toff[i] = (int)(r * L) + (p ^ (r & (TCH - 1))) * 8;   // r*L < 2^31: checked on the host
-    }
     const bf16* Qb = a.Q + base * D;
     const bf16* dOb = a.dO + base * D;
-    const bf16* Qtb = a.Qt + base * D;
-    const bf16* dOtb = a.dOt + base * D;
     auto stage_ptr = [&](auto st) -> char* { return decltype(st)::value == 0 ? lds_a : lds_b; };
     auto dma = [&](int j, auto st) {
         const int64_t r0 = (jb0 + j) * kBwdQB;
@@ -217,25 +230,19 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
             __builtin_amdgcn_global_load_lds(static_cast<const void*>(dOb + r0 * D + roff[i]),
                                              (__attribute__((address_space(3))) void*)(S + R_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < T_PER_T; ++i) {
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Qtb + r0 + toff[i]),
-                                             (__attribute__((address_space(3))) void*)(S + 2 * R_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(dOtb + r0 + toff[i]),
-                                             (__attribute__((address_space(3))) void*)(S + 2 * R_BYTES + T_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
-        }
         if (wave == 0) {   // lanes 0-15: lse, 16-31: delta, 32-63: a copy of lse into the padding
             const float* src = (lane & 16) && lane < 32 ? a.dlt : a.lse;
             __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + base + r0 + 4 * (lane & 15)),
-                                             (__attribute__((address_space(3))) void*)(S + 2 * R_BYTES + 2 * T_BYTES), 16, 0, 0);
+                                             (__attribute__((address_space(3))) void*)(S + 2 * R_BYTES), 16, 0, 0);
         }
     };
 
     // One sub-step of RS rows against the wave's keys; `masked` (uniform)
     // applies the causal test, which only sub-steps whose rows reach the
-    // wave's keys need.
-    auto sub = [&](int64_t r0, int h, const char* Qs, const char* dOs, const char* Qts, const char* dOts,
-                   const char* aux, bool masked) {
+    // wave's keys need. (Inlined by force: an outlined call would keep the
+    // accumulators it updates in scratch memory.)
+    auto sub = [&](int64_t r0, int h, const char* Qs, const char* dOs, const char* aux,
+                   bool masked) __attribute__((always_inline)) {
         f32x4 s[QBS][KB], dp[QBS][KB];
         f32x4 nls[QBS], ndl[QBS];
 #pragma unroll
@@ -303,9 +310,9 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
                 }
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                const int c = cb * 16 + l16, ch = 4 * j32 + q4;
-                const Frag<bf16> of = ld_frag<bf16>(dOts + v_chunk_off<TCH>(c, ch));
-                const Frag<bf16> qf = ld_frag<bf16>(Qts + v_chunk_off<TCH>(c, ch));
+                // dO^T and Q^T: column cb*16 + l16, rows 32*j32 + 8*q4 .. +7
+                const Frag<bf16> of = ld_frag_tr<QCH>(dOs, 32 * j32, cb * 16, lane);
+                const Frag<bf16> qf = ld_frag_tr<QCH>(Qs, 32 * j32, cb * 16, lane);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     dvt[cb][kb] = mma16(of, pf[kb], dvt[cb][kb]);
@@ -318,16 +325,14 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     // One staged step. Edge steps (rows whose tokens reach the workgroup's
     // keys) test each sub-step for keys after every row (skip) or after some
     // row (causal mask); the others need neither and run branch-free.
-    auto step = [&](int j, auto st, auto edge) {
+    auto step = [&](int j, auto st, auto edge) __attribute__((always_inline)) {
         constexpr int SI = decltype(st)::value;
         if (j + 1 < n_steps) dma(j + 1, StageC<SI ^ 1>{});
         const int64_t r0 = (jb0 + j) * kBwdQB;
         const char* S = stage_ptr(st);
         const char* Qs = S;
         const char* dOs = S + R_BYTES;
-        const char* Qts = S + 2 * R_BYTES;
-        const char* dOts = Qts + T_BYTES;
-        const char* aux = dOts + T_BYTES;
+        const char* aux = S + 2 * R_BYTES;
 #pragma unroll
         for (int h = 0; h < NSUB; ++h) {       // rows RS*h .. RS*h + RS-1 of the step
             if constexpr (decltype(edge)::value) {
@@ -335,9 +340,9 @@ void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
                 // exactly when rho < key * Rg: the causal tests need no division.
                 const int64_t rlo = r0 + kBwdRS * h;
                 if (rlo + kBwdRS - 1 < (int64_t)kw * Rg || rlo >= Lreal) continue;   // every key after every row's token
-                sub(r0, h, Qs, dOs, Qts, dOts, aux, rlo < (int64_t)(kw + kBwdKW - 1) * Rg);
+                sub(r0, h, Qs, dOs, aux, rlo < (int64_t)(kw + kBwdKW - 1) * Rg);
             } else {
-                sub(r0, h, Qs, dOs, Qts, dOts, aux, false);
+                sub(r0, h, Qs, dOs, aux, false);
             }
         }
         __syncthreads();
@@ -395,12 +400,10 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
     constexpr int DK = D / 32;
     constexpr int CB = D / 16;
     constexpr int KCH = D / 8;                 // chunks per K / V row
-    constexpr int VCH = BKV / 8;               // chunks per K^T row
     constexpr int K_BYTES = BKV * D * 2;
-    constexpr int STAGE = 3 * K_BYTES;
+    constexpr int STAGE = 2 * K_BYTES;
     constexpr int K_PER_T = BKV * KCH / NT;
-    constexpr int T_PER_T = D * VCH / NT;
-    static_assert(BKV * KCH % NT == 0 && D * VCH % NT == 0, "tiles split evenly over the threads");
+    static_assert(BKV * KCH % NT == 0, "tiles split evenly over the threads");
     __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
     __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
@@ -449,21 +452,13 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) dqt[cb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t vrow = (int64_t)a.rs.Bt * a.Tpad;
     const bf16* Kg = a.K + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
     const bf16* Vg = a.V + ((int64_t)g * a.rs.Bt + b) * a.Tpad * D;
-    const bf16* Ktg = a.Kt + (int64_t)g * D * vrow + (int64_t)b * a.Tpad;
     int koff[K_PER_T];
-    int64_t toff[T_PER_T];
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
         const int s = tid + NT * i, r = s / KCH, p = s % KCH;
         koff[i] = r * D + (p ^ (((r & 3) | (((r >> 3) & 1) << 2)) & (KCH - 1))) * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < T_PER_T; ++i) {
-        const int s = tid + NT * i, r = s / VCH, p = s % VCH;
-        toff[i] = (int64_t)r * vrow + (p ^ (r & (VCH - 1))) * 8;
     }
     auto stage_ptr = [&](auto st) -> char* { return decltype(st)::value == 0 ? lds_a : lds_b; };
     auto dma = [&](int j, auto st) {
@@ -476,15 +471,11 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
             __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vg + k0 * D + koff[i]),
                                              (__attribute__((address_space(3))) void*)(S + K_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < T_PER_T; ++i)
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(Ktg + k0 + toff[i]),
-                                             (__attribute__((address_space(3))) void*)(S + 2 * K_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
     };
 
     // One sub-step of KS keys against the wave's rows; `masked` (uniform)
-    // applies the causal test.
-    auto sub = [&](int k0, int h, const char* Ks, const char* Vs, const char* Kts, bool masked) {
+    // applies the causal test. (Inlined by force, as in the dK/dV kernel.)
+    auto sub = [&](int k0, int h, const char* Ks, const char* Vs, bool masked) __attribute__((always_inline)) {
         f32x4 s[KBS][QBW], dp[KBS][QBW];
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk)
@@ -530,7 +521,8 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
                 }
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                const Frag<bf16> ktf = ld_frag<bf16>(Kts + v_chunk_off<VCH>(cb * 16 + l16, 4 * kc + q4));
+                // K^T: row cb*16 + l16 (a column of K), keys 32*kc + 8*q4 .. +7
+                const Frag<bf16> ktf = ld_frag_tr<KCH>(Ks, 32 * kc, cb * 16, lane);
 #pragma unroll
                 for (int qb = 0; qb < QBW; ++qb) dqt[cb][qb] = mma16(ktf, sf[qb], dqt[cb][qb]);
             }
@@ -540,21 +532,20 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
     // One staged key tile. Edge tiles (keys that reach the workgroup's first
     // token) test each sub-step for keys after every row of the wave (skip)
     // or after some row (causal mask); the others run branch-free.
-    auto tile = [&](int j, auto st, auto edge) {
+    auto tile = [&](int j, auto st, auto edge) __attribute__((always_inline)) {
         constexpr int SI = decltype(st)::value;
         if (j + 1 < n_kv) dma(j + 1, StageC<SI ^ 1>{});
         const int k0 = j * BKV;
         const char* Ks = stage_ptr(st);
         const char* Vs = Ks + K_BYTES;
-        const char* Kts = Vs + K_BYTES;
 #pragma unroll
         for (int h = 0; h < BKV / KS; ++h) {     // keys KS*h .. KS*h + KS-1 of the tile
             if constexpr (decltype(edge)::value) {
                 const int kh = k0 + KS * h;
                 if (kh > t_last) continue;
-                sub(k0, h, Ks, Vs, Kts, kh + KS - 1 > t_first);   // a key may lie above a row's token
+                sub(k0, h, Ks, Vs, kh + KS - 1 > t_first);   // a key may lie above a row's token
             } else {
-                sub(k0, h, Ks, Vs, Kts, false);
+                sub(k0, h, Ks, Vs, false);
             }
         }
         __syncthreads();

@@ -172,8 +172,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
 //                       dw[n,g,r] = <O, dC_weighted>;
 //   shared row:         dO = dC_shared;
 // and delta = <dO, O> (with the bf16 dO the attention kernels use). Writes
-// Q and dO row-major (rows of the row space) and transposed ([d][rows] per
-// sequence), -delta, and for padding rows zero Q / dO / delta and a negated
+// Q and dO row-major (rows of the row space), -delta, and for padding rows
+// zero Q / dO / delta and a negated
 // log-sum-exp of -inf (probability 0), so the attention kernels read whole
 // tiles without tests.
 // Grid: (row blocks of 64, G*Bt). 256 threads; d/8 lanes per row.
@@ -185,9 +185,7 @@ struct PrepArgs {
     const bf16* dC;       // [N, ldc]
     const float* w;       // [N, G*k]
     bf16* Qc;             // [rows][d]
-    bf16* Qt;             // per sequence [d][L]
     bf16* dOc;
-    bf16* dOt;
     float* lse;           // [rows] minus the log2 log-sum-exp (padding rows set here)
     float* dlt;           // [rows] minus delta
     float* dw;            // [N, G*k]
@@ -200,8 +198,6 @@ template <int D>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int RPP = 256 / CPR;             // rows per pass
-    __shared__ bf16 qs[64][D + 2];
-    __shared__ bf16 ds[64][D + 2];
     const int tid = threadIdx.x;
     const int gb = blockIdx.y, g = gb / a.rs.Bt, b = gb % a.rs.Bt;
     const int Rg = rs_R(a.rs, g);
@@ -261,26 +257,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         }
         store8(a.Qc + (base + rho) * a.d + 8 * cc, q);
         store8(a.dOc + (base + rho) * a.d + 8 * cc, dO);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            qs[rr][8 * cc + i] = (bf16)q[i];
-            ds[rr][8 * cc + i] = (bf16)dO[i];
-        }
-    }
-    __syncthreads();
-    // Transposed copies: column c of the 64-row block, 8 rows per store.
-    bf16* qt = a.Qt + base * a.d;
-    bf16* dt = a.dOt + base * a.d;
-    for (int u = tid; u < D * 8; u += 256) {
-        const int c = u >> 3, j = (u & 7) * 8;
-        bf16x8 vq, vd;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            vq[i] = qs[j + i][c];
-            vd[i] = ds[j + i][c];
-        }
-        *reinterpret_cast<bf16x8*>(qt + (int64_t)c * L + rho0 + j) = vq;
-        *reinterpret_cast<bf16x8*>(dt + (int64_t)c * L + rho0 + j) = vd;
     }
 }
 

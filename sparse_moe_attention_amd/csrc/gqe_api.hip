@@ -352,7 +352,7 @@ struct TrainWs {
     int64_t rows, Npad, ccat, ccat_pad, col_k, col_v, col_qsh, col_lg;
     int n_cs, ns_wo, ks_wo, ns_w, ks_w;
     // Forward state (lse) and backward buffers, after the forward's own layout.
-    size_t lse, dlt, Qc, Qt, dOc, dOt, dw, dz, p, cs, dC, WoT, WcT, xT, doT, CT, Kt, V, dY, dYt, part, total;
+    size_t lse, dlt, Qc, dOc, dw, dz, p, cs, dC, WoT, WcT, xT, doT, CT, V, dY, dYt, part, total;
 };
 
 constexpr int kRowPad = kBwdDqBQMax > 256 ? kBwdDqBQMax : 256;   // row-space runs pad to whole dQ row tiles
@@ -401,9 +401,7 @@ TrainWs train_layout(const Dims& d) {
     L.lse = take(rows * 4);
     L.dlt = take(rows * 4);
     L.Qc = take(rows * d.d * 2);
-    L.Qt = take(rows * d.d * 2);
     L.dOc = take(rows * d.d * 2);
-    L.dOt = take(rows * d.d * 2);
     L.dw = take((size_t)d.N * d.GK * 4);
     L.dz = take((size_t)d.N * d.E * 4);
     L.p = take((size_t)d.N * d.E * 4);
@@ -414,7 +412,6 @@ TrainWs train_layout(const Dims& d) {
     L.xT = take((size_t)d.D * L.Npad * 2);
     L.doT = take((size_t)d.D * L.Npad * 2);
     L.CT = take((size_t)SD * L.Npad * 2);
-    L.Kt = take((size_t)d.G * d.d * d.B * d.Tpad * 2);
     L.V = take((size_t)d.G * d.B * d.Tpad * d.d * 2);
     L.dY = take((size_t)d.N * L.ccat_pad * 2);
     L.dYt = take((size_t)L.ccat * L.Npad * 2);
@@ -472,8 +469,8 @@ void run_wgrad(const void* A, int64_t lda, int64_t rows, const void* W, int64_t 
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, r);
 }
 
-// Zero K rows and V^T columns of tokens in [T, Tpad): the backward's
-// transposed copies then hold zeros there.
+// Zero K rows and V^T columns of tokens in [T, Tpad): K (whose columns the dQ
+// kernel contracts over keys) and the row-major V copy then hold zeros there.
 __global__ void kv_pad_kernel(bf16* K, bf16* Vt, int64_t T, int64_t Tpad, int Bt, int d) {
     const int g = blockIdx.x / Bt, b = blockIdx.x % Bt;
     const int64_t n_pad = Tpad - T;
@@ -506,7 +503,6 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
     const GqeWs F = gqe_layout(d);
     const TrainWs L = train_layout(d);
     if (ws_bytes < L.total) return GQE_ERR_WORKSPACE;
-    if ((int64_t)d.d * L.rs.Lx >= ((int64_t)1 << 31)) return GQE_ERR_SHAPE;   // 32-bit staging offsets
     hipStream_t st = (hipStream_t)stream;
     const Marks mk{events, st};
     const int64_t SD = (int64_t)d.slots * d.d, N = d.N, D = d.D, dh = d.d;
@@ -529,7 +525,6 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
     if (d.Tpad > d.T)
         hipLaunchKernelGGL(kv_pad_kernel, dim3((unsigned)(d.G * d.B)), dim3(256), 0, st, B(F.K), B(F.Vt), d.T, d.Tpad,
                            (int)d.B, d.d);
-    run_transpose(B(F.K), dh, vrow, dh, B(L.Kt), vrow, vrow, dh, d.G, vrow * dh, vrow * dh, st);
     run_transpose(B(F.Vt), vrow, dh, vrow, B(L.V), dh, dh, vrow, d.G, vrow * dh, vrow * dh, st);
     mk.at(1);
 
@@ -548,7 +543,7 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
         PrepArgs pa;
         pa.Qr = B(F.Qr); pa.Qsh = B(F.Qsh); pa.C = B(F.C); pa.dC = B(L.dC);
         pa.w = F32(F.w);
-        pa.Qc = B(L.Qc); pa.Qt = B(L.Qt); pa.dOc = B(L.dOc); pa.dOt = B(L.dOt);
+        pa.Qc = B(L.Qc); pa.dOc = B(L.dOc);
         pa.lse = F32(L.lse); pa.dlt = F32(L.dlt); pa.dw = F32(L.dw);
         pa.rs = L.rs;
         pa.ldc = SD;
@@ -590,9 +585,9 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
 
     // Attention backward.
     AttnBwdArgs ab;
-    ab.Q = B(L.Qc); ab.Qt = B(L.Qt); ab.dO = B(L.dOc); ab.dOt = B(L.dOt);
+    ab.Q = B(L.Qc); ab.dO = B(L.dOc);
     ab.lse = F32(L.lse); ab.dlt = F32(L.dlt);
-    ab.K = B(F.K); ab.V = B(L.V); ab.Kt = B(L.Kt);
+    ab.K = B(F.K); ab.V = B(L.V);
     ab.dY = B(L.dY);
     ab.idx = (const int32_t*)at(ws, F.idx);
     ab.ldy = L.ccat_pad;
