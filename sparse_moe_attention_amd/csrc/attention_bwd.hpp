@@ -14,8 +14,8 @@
 // score products start from. dK = ln(2) * dS^T Qs.
 //
 // Two kernels, no atomics (deterministic):
-//   * attn_bwd_dkdv_kernel: one workgroup per (group, sequence, 256 keys at
-//     d = 64, 128 at d = 32);
+//   * attn_bwd_dkdv_kernel: one workgroup per (group, sequence, 128 keys),
+//     two per CU;
 //     each wave keeps 32 keys' K and V as resident MFMA operands and
 //     accumulates their dK^T, dV^T over every query row at or after the
 //     keys, 64 rows per step staged in LDS (Q and dO row-major, lse and
@@ -67,16 +67,18 @@ struct AttnBwdArgs {
 // their LDS at 32 KB, 32-key sub-steps their registers at 168): the waves
 // sharing a SIMD then come from independent workgroups and overlap one
 // another's exponent and product phases (10% faster than one eight-wave
-// workgroup of 128-key tiles per CU at T = 32K). The dK/dV kernel at d = 64
-// runs one eight-wave workgroup of 256 keys per CU: each staged Q/dO step
-// then serves twice the keys, which halves the staged traffic (T = 1M:
-// 4.25 -> 3.42 s, where the query rows no longer stay in L2; 1-2.5% at
-// 16K-32K; 3% slower on the 0.12 ms kernel at T = 2048).
+// workgroup of 128-key tiles per CU at T = 32K). The dK/dV kernel runs two
+// four-wave workgroups of 128 keys per CU (252 registers: two waves per
+// SIMD), for the same reason: against one eight-wave workgroup of 256 keys
+// per CU, whose staged Q/dO steps serve twice the keys, it measured 4.5%
+// faster at T = 32K, 15% at T = 2048 and even at T = 1M, where the staged
+// traffic had made the eight-wave form 20% faster while the transposed
+// copies of Q and dO were staged as well.
 #ifndef GQE_BWD_KW
 #define GQE_BWD_KW 32
 #endif
 #ifndef GQE_BWD_NW
-#define GQE_BWD_NW 8
+#define GQE_BWD_NW 4
 #endif
 #ifndef GQE_BWD_RS
 #define GQE_BWD_RS 64
@@ -100,8 +102,9 @@ struct AttnBwdArgs {
 #define GQE_BWD_DQ_BKV 64
 #endif
 constexpr int kBwdKW = GQE_BWD_KW;         // keys per wave (dK/dV kernel)
-// Waves per dK/dV workgroup: head width 32 stages half the bytes per step,
-// which 512 threads do not split evenly, so it keeps 4 waves.
+// Waves per dK/dV workgroup (an eight-wave form exists for d = 64 only: head
+// width 32 stages half the bytes per step, which 512 threads do not split
+// evenly).
 template <int D> constexpr int bwd_nw() { return D == 64 ? GQE_BWD_NW : 4; }
 template <int D> constexpr int bwd_bk() { return kBwdKW * bwd_nw<D>(); }   // keys per dK/dV workgroup
 constexpr int kBwdBKMax = kBwdKW * (GQE_BWD_NW > 4 ? GQE_BWD_NW : 4);

@@ -27,8 +27,10 @@ int main() {
                         rs.Bt = Bt;
                         rs.R = R;
                         rs.s0 = s0;
-                        for (int kind = 0; kind < 2; ++kind) {   // 0: dK/dV (256 keys), 1: dQ (128 rows)
-                            const int64_t BS = kind == 0 ? 256 : 128;
+                        // 0: dK/dV (128 keys), 1: dK/dV (256 keys), 2: dQ (128 rows)
+                        for (int cfg = 0; cfg < 3; ++cfg) {
+                            const int kind = cfg < 2 ? 0 : 1;
+                            const int64_t BS = cfg == 1 ? 256 : 128;
                             const int64_t n_r = kind == 0 ? (T + BS - 1) / BS : ((int64_t)T * R + BS - 1) / BS;
                             const int64_t n_x = kind == 0 ? n_r : ((int64_t)T * (R + 1) + BS - 1) / BS;
                             const int64_t stride = n_x > n_r ? n_x : n_r;

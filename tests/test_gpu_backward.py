@@ -244,7 +244,7 @@ def test_backward_long_shape_last_rows():
     with no balancing loss. Every gradient then comes from those rows'
     attention over their whole causal prefixes: dQ of the four rows from the
     256-row, 128-key dQ tiles at offsets near 262K, dK and dV of every key
-    block up to the end from the eight-wave dK/dV kernel, and the projections'
+    block up to the end from the dK/dV kernel, and the projections'
     sums over all tokens. The fp64 row-by-row backward oracle computes exactly
     these gradients, so all of them are compared at the parity bar."""
     s = Shape(B=1, T=262144 + 64, D=128, G=2, M=2, k=1, d=64)
