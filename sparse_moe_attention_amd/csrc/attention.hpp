@@ -90,6 +90,9 @@ struct AttnShape {
 #endif
 using AttnShort = AttnShape<GQE_ATTN_SHORT_SHAPE>;
 using AttnLong = AttnShape<32, 8, 128, 2>;
+// fp32 layers: the short tile with registers for two waves per SIMD (fp32
+// fragments are twice the registers; at d = 64 three would not fit).
+using AttnShortF32 = AttnShape<32, 4, 64, 2>;
 constexpr float kLazyRescale = 8.f;   // log2 units the running max may lag by
 
 // Maximum that propagates NaN (IEEE maximum): gfx950 has it as v_maximum3_f32

@@ -35,7 +35,7 @@ namespace {
 
 // Sequence padding of the K / V^T buffers: whole key tiles of the forward
 // and whole key blocks of the dK/dV kernel (its waves read their keys' rows).
-constexpr int kKVPad = std::max({AttnShort::BKV, AttnLong::BKV, kBwdBKMax, kBwdBKVMax});
+constexpr int kKVPad = std::max({AttnShort::BKV, AttnShortF32::BKV, AttnLong::BKV, kBwdBKMax, kBwdBKVMax});
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -226,7 +226,7 @@ void run_grouped_q(const Dims& d, const void* x, const void* Wq, void* Qr, const
 // Attention tile shape by sequence length: AttnShort up to T = 256K, AttnLong
 // beyond (measured on the 8-group d = 64 layer: AttnShort 1-3% ahead from
 // T = 64K to 256K, even at 512K, AttnLong 34% ahead at 1M). fp32 layers (the
-// small reference configuration) always take AttnShort.
+// small reference configuration) always take the short tile (AttnShortF32).
 #ifndef GQE_ATTN_LONG_T
 #define GQE_ATTN_LONG_T 262144
 #endif
@@ -247,7 +247,7 @@ void run_attention(const Dims& d, AttnArgs& a, hipStream_t st) {
     a.Tpad = d.Tpad;
     a.Bt = (int)d.B;
     a.G = d.G;
-    if (d.f32) launch_attention<float, AttnShort>(d, a, st);
+    if (d.f32) launch_attention<float, AttnShortF32>(d, a, st);
     else if (d.T > kAttnLongT) launch_attention<bf16, AttnLong>(d, a, st);
     else launch_attention<bf16, AttnShort>(d, a, st);
 }
