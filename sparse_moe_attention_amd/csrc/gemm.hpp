@@ -4,9 +4,10 @@
 //     (dense K and V of every group, the shared head's Q, the router logits),
 //     each block with its own output buffer and layout; also the output
 //     projection and the dense-GQA Q projection;
-//   * grouped_q_kernel: the sparse Q projection, one (token chunk, expert)
-//     segment per workgroup, rows gathered through the permutation and
-//     scattered back to the dense [token, group, rank, d] layout.
+//   * grouped_q_kernel: the sparse Q projection, one tile of one expert's
+//     segment of the permutation per workgroup, rows gathered through the
+//     permutation and scattered back to the dense [token, group, rank, d]
+//     layout.
 // Projections are dense contractions, so they run on MFMA: WM x WN waves, each wave a (BM/WM) x (BN/WN) block of 16x16 MFMA tiles;
 // the K loop stages 128-byte rows of A and B through double-buffered LDS.
 #pragma once
