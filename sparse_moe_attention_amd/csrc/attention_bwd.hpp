@@ -596,3 +596,174 @@ void attn_bwd_dq_kernel(AttnBwdArgs a) {
 }
 
 }  // namespace gqe
+
+namespace gqe {
+
+// ---------------------------------------------------------------------------
+// Weight gradient of the routed query projections, grouped by expert over the
+// forward's permutation (every picked expert owns its query projection,
+// FrontiersMind GQE article, part 4, so its gradient sums over the tokens
+// that picked it):
+//   dWq[e*d + i][c] = sum over the tokens n of expert e's segment of
+//                     dQ_e[n][i] * x[n][c],
+// with dQ_e[n] read from the gradient matrix dY (columns e*d .. e*d + d - 1 of
+// row n) and x[n] from the layer input. Only the G*k picks per token enter,
+// not the M experts' columns of dY (zero where unpicked). The contraction
+// runs over gathered tokens, so both operands are staged token-major and
+// their MFMA fragments come from the transposing LDS read (ld_frag_tr).
+// Workgroup = (split s, expert e, column tile ct): tokens of split s of the
+// expert's segment against 256 columns of x (four waves of 64 x 64; 80 KB of
+// LDS, two workgroups per CU; 64 x 128 tiles at three per CU measured 1-4%
+// slower); every workgroup writes its fp32
+// partial to part[s] (zeros for an empty split), and splitk_reduce_kernel
+// sums the splits in a fixed order (deterministic).
+// ---------------------------------------------------------------------------
+struct GroupDwArgs {
+    const bf16* dY;        // [N][ldy]
+    const bf16* X;         // [N][D]
+    const int32_t* perm;   // permutation row -> token
+    const int32_t* cbase;  // [nC+1][E]: row 0 = segment starts, row nC = segment ends
+    float* part;           // [S][E*d][D]
+    int64_t ldy, split_stride;
+    int32_t D, E, nC, S, n_ct;
+};
+constexpr int kDwBN = 256;     // x columns per workgroup (64 per wave)
+constexpr int kDwBK = 64;      // tokens per staged step
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_dw_kernel(GroupDwArgs a) {
+    constexpr int NT = 256;
+    constexpr int QCH = D / 8;                 // 16-byte chunks per dQ row
+    constexpr int XCH = kDwBN / 8;             // 16-byte chunks per staged x row
+    constexpr int Q_BYTES = kDwBK * D * 2;
+    constexpr int X_BYTES = kDwBK * kDwBN * 2;
+    constexpr int STAGE = Q_BYTES + X_BYTES;
+    constexpr int Q_PER_T = kDwBK * QCH / NT;
+    constexpr int X_PER_T = kDwBK * XCH / NT;
+    constexpr int FM = D / 16;                 // 16-row blocks of the d rows
+    constexpr int FN = 4;                      // 16-column blocks per wave
+    static_assert(kDwBK * QCH % NT == 0 && kDwBK * XCH % NT == 0 && kDwBN == 4 * FN * 16, "dW tile shape");
+    __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
+    __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ct = (int)(blockIdx.x % a.n_ct);
+    const int e = (int)((blockIdx.x / a.n_ct) % a.E);
+    const int s = (int)(blockIdx.x / ((int64_t)a.n_ct * a.E));
+    const int c0 = ct * kDwBN;
+    const int sb = a.cbase[e], se = a.cbase[(int64_t)a.nC * a.E + e];
+    const int len = se - sb;
+    const int per = ((len + a.S - 1) / a.S + kDwBK - 1) / kDwBK * kDwBK;   // whole steps per split
+    const int p0 = sb + min(len, s * per), p1 = sb + min(len, (s + 1) * per);
+    const int n_steps = (p1 - p0 + kDwBK - 1) / kDwBK;
+
+    // Staged chunks of this thread: slot it = tid + NT*i holds chunk it % CH of
+    // row it / CH, which is the row's logical chunk (it % CH) ^ swz(row).
+    auto swz = [](int r) { return (r & 3) | (((r >> 3) & 1) << 2); };
+    int q_off[Q_PER_T], x_off[X_PER_T];
+#pragma unroll
+    for (int i = 0; i < Q_PER_T; ++i) {
+        const int it = tid + NT * i, r = it / QCH;
+        q_off[i] = e * D + ((it % QCH) ^ (swz(r) & (QCH - 1))) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < X_PER_T; ++i) {
+        const int it = tid + NT * i, r = it / XCH;
+        const int c = c0 + ((it % XCH) ^ (swz(r) & (XCH - 1))) * 8;
+        x_off[i] = c < a.D ? c : 0;            // columns past D: any valid column, never stored
+    }
+    // Tokens of this thread's staged rows for the next step to load (rows
+    // past the split repeat its first token; their dQ rows are zeroed in LDS
+    // before use). Fetched one step ahead of their use, so the gathers never
+    // wait on the permutation.
+    int tq[Q_PER_T], tx[X_PER_T];
+    auto fetch_tokens = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < Q_PER_T; ++i) {
+            const int p = p0 + j * kDwBK + (tid + NT * i) / QCH;
+            tq[i] = a.perm[p < p1 ? p : p0];
+        }
+#pragma unroll
+        for (int i = 0; i < X_PER_T; ++i) {
+            const int p = p0 + j * kDwBK + (tid + NT * i) / XCH;
+            tx[i] = a.perm[p < p1 ? p : p0];
+        }
+    };
+    auto stage_ptr = [&](auto st) -> char* { return decltype(st)::value == 0 ? lds_a : lds_b; };
+    auto dma = [&](auto st) {                  // the rows fetch_tokens last fetched
+        char* S = stage_ptr(st);
+#pragma unroll
+        for (int i = 0; i < Q_PER_T; ++i)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.dY + (int64_t)tq[i] * a.ldy + q_off[i]),
+                                             (__attribute__((address_space(3))) void*)(S + (NT * i + 64 * wave) * 16), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < X_PER_T; ++i)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.X + (int64_t)tx[i] * a.D + x_off[i]),
+                                             (__attribute__((address_space(3))) void*)(S + Q_BYTES + (NT * i + 64 * wave) * 16), 16, 0, 0);
+    };
+    // Last step: zero the dQ rows past the split (after the barrier that
+    // published the stage; ends with a barrier).
+    auto fix_tail = [&](int j, auto st) {
+        const int valid = p1 - (p0 + j * kDwBK);
+        if (valid >= kDwBK) return;            // uniform
+        char* S = stage_ptr(st);
+        for (int u = tid; u < kDwBK * QCH; u += NT)
+            if (u / QCH >= valid) *reinterpret_cast<u32x4*>(S + u * 16) = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](int j, auto st) __attribute__((always_inline)) {
+        constexpr int SI = decltype(st)::value;
+        fix_tail(j, st);
+        if (j + 1 < n_steps) {
+            dma(StageC<SI ^ 1>{});
+            if (j + 2 < n_steps) fetch_tokens(j + 2);
+        }
+        const char* Qs = stage_ptr(st);
+        const char* Xs = Qs + Q_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < kDwBK / 32; ++ks) {
+            Frag<bf16> qf[FM], xf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) qf[i] = ld_frag_tr<QCH>(Qs, 32 * ks, 16 * i, lane);
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn) xf[jn] = ld_frag_tr<XCH>(Xs, 32 * ks, 64 * wave + 16 * jn, lane);
+            // x fragment as A: the lane ends with 4 consecutive columns of one d row
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mma16(xf[jn], qf[i], acc[i][jn]);
+        }
+        __syncthreads();    // releases this stage and (waiting for the loads) publishes the next
+    };
+    if (n_steps > 0) {
+        fetch_tokens(0);
+        dma(StageC<0>{});
+        if (n_steps > 1) fetch_tokens(1);
+        __syncthreads();
+        for (int j = 0; j < n_steps; j += 2) {
+            step(j, StageC<0>{});
+            if (j + 1 < n_steps) step(j + 1, StageC<1>{});
+        }
+    }
+    // lane holds dWq row e*D + 16i + l16, columns c0 + 64*wave + 16*jn + 4*(lane/16) .. +3
+    float* out = a.part + (int64_t)s * a.split_stride;
+    const int l16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) {
+        const int c = c0 + 64 * wave + 16 * jn + 4 * q4;
+        if (c >= a.D) continue;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            *reinterpret_cast<f32x4*>(out + (int64_t)(e * D + 16 * i + l16) * a.D + c) = acc[i][jn];
+    }
+}
+
+}  // namespace gqe

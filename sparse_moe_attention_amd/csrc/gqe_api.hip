@@ -351,8 +351,9 @@ struct TrainWs {
     RowSpace rs;
     int64_t rows, Npad, ccat, ccat_pad, col_k, col_v, col_qsh, col_lg;
     int n_cs, ns_wo, ks_wo, ns_w, ks_w;
+    int n_gs, n_gct;          // grouped dWq: splits per expert segment, column tiles
     // Forward state (lse) and backward buffers, after the forward's own layout.
-    size_t lse, dlt, Qc, dOc, dw, dz, p, cs, dC, WoT, WcT, xT, doT, CT, V, dY, dYt, part, total;
+    size_t lse, dlt, Qc, dOc, dw, dz, p, cs, dC, WoT, WcT, xT, doT, CT, V, dY, dYt, part, gpart, total;
 };
 
 constexpr int kRowPad = kBwdDqBQMax > 256 ? kBwdDqBQMax : 256;   // row-space runs pad to whole dQ row tiles
@@ -391,9 +392,20 @@ TrainWs train_layout(const Dims& d) {
     L.n_cs = (int)((d.N + kColsumRows - 1) / kColsumRows);
     const int64_t SD = (int64_t)d.slots * d.d;
     const int64_t t_wo = ((d.D + 127) / 128) * ((SD + 127) / 128);
-    const int64_t t_w = ((L.ccat + 127) / 128) * ((d.D + 127) / 128);
+    // The dense weight-gradient GEMM covers dY's columns from dK on; the
+    // routed queries' dWq is the grouped kernel's.
+    const int64_t wrows = L.ccat - L.col_k;
+    const int64_t t_w = ((wrows + 127) / 128) * ((d.D + 127) / 128);
     pick_splits(t_wo, L.Npad, &L.ns_wo, &L.ks_wo);
     pick_splits(t_w, L.Npad, &L.ns_w, &L.ks_w);
+    // Grouped dWq: about 1024 workgroups, segments split into runs of at
+    // least 256 picks on average.
+    L.n_gct = (int)((d.D + kDwBN - 1) / kDwBN);
+    {
+        const int64_t base = (int64_t)d.E * L.n_gct;
+        const int64_t avg = d.N * d.GK / d.E;
+        L.n_gs = (int)std::max<int64_t>(1, std::min<int64_t>((1024 + base - 1) / base, avg / 256));
+    }
 
     size_t o = gqe_layout(d).total;
     auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
@@ -414,8 +426,9 @@ TrainWs train_layout(const Dims& d) {
     L.CT = take((size_t)SD * L.Npad * 2);
     L.V = take((size_t)d.G * d.B * d.Tpad * d.d * 2);
     L.dY = take((size_t)d.N * L.ccat_pad * 2);
-    L.dYt = take((size_t)L.ccat * L.Npad * 2);
-    L.part = take(std::max((size_t)L.ns_wo * d.D * SD, (size_t)L.ns_w * L.ccat * d.D) * 4);
+    L.dYt = take((size_t)wrows * L.Npad * 2);
+    L.part = take(std::max((size_t)L.ns_wo * d.D * SD, (size_t)L.ns_w * wrows * d.D) * 4);
+    L.gpart = take((size_t)L.n_gs * d.E * d.d * d.D * 4);
     L.total = o;
     return L;
 }
@@ -615,8 +628,9 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
     }
     mk.at(5);
 
-    // dx = dY W_cat, dW_cat = dY^T x.
-    run_transpose(B(L.dY), L.ccat_pad, N, L.ccat, B(L.dYt), L.Npad, L.Npad, L.ccat, 1, 0, 0, st);
+    // dx = dY W_cat, dW_cat = dY^T x (dWq grouped by expert, the rest dense).
+    const int64_t wrows = L.ccat - L.col_k;
+    run_transpose(B(L.dY) + L.col_k, L.ccat_pad, N, wrows, B(L.dYt), L.Npad, L.Npad, wrows, 1, 0, 0, st);
     {
         SegList sl = gemm_base(B(L.dY), L.ccat_pad, N, (int)L.ccat_pad);
         sl.add(B(L.WcT), (int)D, dx, OUT_ROWS_F32, D, nullptr);
@@ -624,12 +638,34 @@ gqe_status bwd_impl(const gqe_shape* s, const void* x, const void* Wr, const voi
     }
     mk.at(6);
     {
-        const RedDst dst[5] = {{dWq, 0, (int64_t)d.E * dh},
-                               {dWk, L.col_k, (int64_t)d.G * dh},
-                               {dWv, L.col_v, (int64_t)d.G * dh},
-                               {dWq_sh, L.col_qsh, dh},
-                               {dWr, L.col_lg, d.E}};
-        run_wgrad(B(L.dYt), L.Npad, L.ccat, B(L.xT), D, L.Npad, L.ns_w, L.ks_w, F32(L.part), dst, 5, st);
+        GroupDwArgs ga;
+        ga.dY = B(L.dY);
+        ga.X = (const bf16*)x;
+        ga.perm = (const int32_t*)at(ws, F.perm);
+        ga.cbase = (const int32_t*)at(ws, F.cbase);
+        ga.part = F32(L.gpart);
+        ga.ldy = L.ccat_pad;
+        ga.split_stride = (int64_t)d.E * dh * D;
+        ga.D = (int32_t)D; ga.E = d.E; ga.nC = (int32_t)d.nC; ga.S = L.n_gs; ga.n_ct = L.n_gct;
+        const dim3 grid((unsigned)((int64_t)L.n_gs * d.E * L.n_gct));
+        if (dh == 64) hipLaunchKernelGGL(grouped_dw_kernel<64>, grid, dim3(256), 0, st, ga);
+        else hipLaunchKernelGGL(grouped_dw_kernel<32>, grid, dim3(256), 0, st, ga);
+        RedArgs r;
+        std::memset(&r, 0, sizeof(r));
+        r.part = F32(L.gpart);
+        r.split_stride = ga.split_stride;
+        r.rows = (int64_t)d.E * dh;
+        r.cols = D;
+        r.n_split = L.n_gs;
+        r.n_dst = 1;
+        r.dst[0] = RedDst{dWq, 0, (int64_t)d.E * dh};
+        const int64_t items = r.rows * (D / 4);
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, r);
+        const RedDst dst[4] = {{dWk, 0, (int64_t)d.G * dh},
+                               {dWv, L.col_v - L.col_k, (int64_t)d.G * dh},
+                               {dWq_sh, L.col_qsh - L.col_k, dh},
+                               {dWr, L.col_lg - L.col_k, d.E}};
+        run_wgrad(B(L.dYt), L.Npad, wrows, B(L.xT), D, L.Npad, L.ns_w, L.ks_w, F32(L.part), dst, 4, st);
     }
     mk.at(7);
     return last_hip();
